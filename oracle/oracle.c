@@ -1,0 +1,295 @@
+/*
+ * Plain CPU oracle for the block-quantized projection matmul.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this code: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no source, header, table or helper with the
+ * HIP library; both sides read the same seeded input bytes and nothing else.
+ *
+ * Deliberately slow and literal: every function follows the definition in
+ * the order the pages state it, with no blocking, fusion or reordering.
+ * Built with -O2 -fno-fast-math -ffp-contract=off so every float operation
+ * is the one written (no fused multiply-add, no reassociation).
+ *
+ * Sources (memra-engine docs.rs source pages):
+ *  - Q8_0 weight block = fp16 scale + 32 int8 quants, 34 bytes; a row is
+ *    in_f/32 blocks: "decode_kernel_census.rs" (0.113.0), fn q8;
+ *    "accprobe_bench.rs" (0.124.1), fn synth_w_q8_0.
+ *  - q8_1 activation = one int8 per column + a pair of f32 per 32-block:
+ *    "decode_kernel_census.rs", fn q8.
+ *  - int8 quantization d = amax/127, q = clamp(round(v/d), -127, 127) with
+ *    Rust's round (half away from zero): "f16_ffi.rs" (0.81.0), fn
+ *    try_f16_gemm (the W8A8 simulation arm); "an int8 quantizer emits +-127
+ *    at every block amax": "accprobe_bench.rs", module doc.
+ *  - s32 accumulate per 32-block, folded into f32 by the two scales:
+ *    "accprobe_bench.rs", module doc (the floor folds every k32).
+ *  - e4m3: 0x7F magnitude is NaN ("accprobe_bench.rs" module doc;
+ *    "fp8_ffi.rs" (0.70.0), FP8_MMQ_NAN_OK doc), codes 0x01-0x07 are
+ *    denormals ("accprobe_bench.rs", fn synth_w_q8_0 doc); activation scale
+ *    amax/448 per batch, one scalar, folded with weight_scale into a device
+ *    scalar read by the GEMM; scale block [0]=amax, [1]=quant mul,
+ *    [2]=folded scale ("fp8_ffi.rs", module doc and Fp8Scratch doc).
+ *
+ * Readings where the pages are silent are listed beside each function.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define QK 32
+#define Q8_0_BYTES 34
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* IEEE 754 binary16 -> binary32, exact (normals, subnormals, inf, NaN). */
+float oracle_fp16_to_f32(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)f, -24);               /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(1024 + f), e - 25);   /* (1 + f/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Round half away from zero (Rust's f32::round), written out. */
+static float round_half_away(float v) {
+    float a = fabsf(v);
+    float fl = floorf(a);
+    float r = (a - fl >= 0.5f) ? fl + 1.0f : fl;
+    return v < 0.0f ? -r : r;
+}
+
+/*
+ * q8_1 activation quantization, per (token, 32-block):
+ *   amax = max |x_i|;  d = amax / 127 (f32 division);
+ *   q_i = clamp(round_half_away(x_i / d), -127, 127) (f32 division);
+ *   s = d * (float)sum(q_i)  -- the second value of the scale pair.
+ * Readings: amax == 0 gives d = 0, q = 0, s = 0 (the W8A8 arm leaves an
+ * all-zero row untouched); the second pair value is d times the quant sum
+ * (the pages only say "a pair", the Q8_0 path never reads it).
+ * xds layout: [m][k/32][2] = (d, s).
+ */
+void oracle_q8_1_quantize(const float *x, int8_t *xq, float *xds, int64_t m, int64_t k) {
+    int64_t nb = k / QK;
+    for (int64_t t = 0; t < m; t++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *blk = x + t * k + b * QK;
+            int8_t *q = xq + t * k + b * QK;
+            float amax = 0.0f;
+            for (int i = 0; i < QK; i++) {
+                float a = fabsf(blk[i]);
+                if (a > amax) amax = a;
+            }
+            float d = amax / 127.0f;
+            int sum = 0;
+            for (int i = 0; i < QK; i++) {
+                float r = 0.0f;
+                if (amax > 0.0f) {
+                    r = round_half_away(blk[i] / d);
+                    if (r > 127.0f) r = 127.0f;
+                    if (r < -127.0f) r = -127.0f;
+                }
+                q[i] = (int8_t)r;
+                sum += (int)r;
+            }
+            xds[2 * (t * nb + b) + 0] = d;
+            xds[2 * (t * nb + b) + 1] = d * (float)sum;
+        }
+    }
+}
+
+/* Weight block accessors: scale in bytes 0..1 (little-endian fp16), quants in 2..33. */
+static float q8_0_scale(const uint8_t *blk) {
+    return oracle_fp16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+}
+
+/*
+ * Integer block sums S[t][n][b] = sum_i q_w[n][b][i] * q_x[t][b][i] (int32).
+ */
+void oracle_q8_0_block_sums(const uint8_t *w, int64_t row_bytes, const int8_t *xq,
+                            int64_t m, int64_t k, int64_t n, int32_t *S) {
+    int64_t nb = k / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++) {
+        for (int64_t t = 0; t < m; t++) {
+            for (int64_t b = 0; b < nb; b++) {
+                const uint8_t *blk = w + r * row_bytes + b * Q8_0_BYTES;
+                int32_t s = 0;
+                for (int i = 0; i < QK; i++)
+                    s += (int32_t)(int8_t)blk[2 + i] * (int32_t)xq[t * k + b * QK + i];
+                S[(t * n + r) * nb + b] = s;
+            }
+        }
+    }
+}
+
+/* One output element: y = sum_b d_w * d_x * S_b in fp64; T = sum_b |d_w * d_x * S_b|. */
+static void q8_0_dot(const uint8_t *wrow, const int8_t *xrow, const float *xdsrow, int64_t nb,
+                     double *y, double *tabs) {
+    double acc = 0.0, aabs = 0.0;
+    for (int64_t b = 0; b < nb; b++) {
+        const uint8_t *blk = wrow + b * Q8_0_BYTES;
+        int32_t s = 0;
+        for (int i = 0; i < QK; i++)
+            s += (int32_t)(int8_t)blk[2 + i] * (int32_t)xrow[b * QK + i];
+        double term = (double)q8_0_scale(blk) * (double)xdsrow[2 * b] * (double)s;
+        acc += term;
+        aabs += fabs(term);
+    }
+    *y = acc;
+    *tabs = aabs;
+}
+
+/*
+ * Q8_0 x q8_1 matmul, y[t][n] = sum_b d_w[n][b] * d_x[t][b] * S[t][n][b], in fp64.
+ * w: [n] rows of row_bytes bytes (first k/32*34 used); xq [m][k]; xds [m][k/32][2].
+ * Outputs y and T = sum of |terms|, both [m][n].
+ */
+void oracle_q8_0_matmul(const uint8_t *w, int64_t row_bytes, const int8_t *xq, const float *xds,
+                        int64_t m, int64_t k, int64_t n, double *y, double *tabs) {
+    int64_t nb = k / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t t = 0; t < m; t++)
+            q8_0_dot(w + r * row_bytes, xq + t * k, xds + t * nb * 2, nb,
+                     &y[t * n + r], &tabs[t * n + r]);
+}
+
+/* Same as oracle_q8_0_matmul for a list of (token, row) pairs only. */
+void oracle_q8_0_matmul_sampled(const uint8_t *w, int64_t row_bytes, const int8_t *xq,
+                                const float *xds, int64_t k, int64_t npairs,
+                                const int64_t *tok, const int64_t *row, double *y, double *tabs) {
+    int64_t nb = k / QK;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npairs; p++)
+        q8_0_dot(w + row[p] * row_bytes, xq + tok[p] * k, xds + tok[p] * nb * 2, nb,
+                 &y[p], &tabs[p]);
+}
+
+/*
+ * OCP E4M3FN decode: sign | 4-bit exponent (bias 7) | 3-bit mantissa.
+ * Exponent field 0 is subnormal (m * 2^-9); magnitude 0x7F is NaN; no infinity.
+ */
+float oracle_e4m3_decode(uint8_t c) {
+    int sign = c >> 7;
+    int e = (c >> 3) & 15;
+    int mant = c & 7;
+    float v;
+    if ((c & 0x7F) == 0x7F)
+        return NAN;
+    if (e == 0)
+        v = ldexpf((float)mant, -9);
+    else
+        v = ldexpf((float)(8 + mant), e - 10);   /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/*
+ * f32 -> E4M3FN: clamp to [-448, 448], then round to the nearest representable
+ * magnitude, ties to the even code (even mantissa), searching every finite
+ * non-negative code.  The sign of x is kept, so -0 and negative values that
+ * round to zero give 0x80.  NaN codes are never produced.
+ * Readings: saturation (clamp before rounding) and round-to-nearest-even are
+ * the plainest reading; the pages fix only the amax/448 scale and the NaN code.
+ */
+uint8_t oracle_e4m3_encode(float x) {
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    float a = fabsf(x);
+    if (a > 448.0f) a = 448.0f;
+    uint8_t best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; c++) {
+        double d = fabs((double)oracle_e4m3_decode((uint8_t)c) - (double)a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best_d = d;
+            best = (uint8_t)c;
+        }
+    }
+    return sign | best;
+}
+
+void oracle_e4m3_encode_array(const float *x, uint8_t *out, int64_t count) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; i++) out[i] = oracle_e4m3_encode(x[i]);
+}
+
+/*
+ * Per-batch e4m3 activation quantization:
+ *   amax = max |x| over all m*k values;
+ *   mul = 448 / amax, x_scale = amax / 448 (f32; both 0 when amax == 0);
+ *   folded = x_scale * w_scale (f32);
+ *   xq = encode(x * mul) with the product in f32.
+ * scales = {amax, mul, folded, x_scale}.
+ */
+void oracle_e4m3_quantize_amax(const float *x, uint8_t *xq, float *scales, float w_scale,
+                               int64_t m, int64_t k) {
+    int64_t count = m * k;
+    float amax = 0.0f;
+    for (int64_t i = 0; i < count; i++) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    float mul = 0.0f, xs = 0.0f;
+    if (amax > 0.0f) {
+        mul = 448.0f / amax;
+        xs = amax / 448.0f;
+    }
+    float folded = xs * w_scale;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; i++) {
+        float v = x[i] * mul;
+        xq[i] = oracle_e4m3_encode(v);
+    }
+    scales[0] = amax;
+    scales[1] = mul;
+    scales[2] = folded;
+    scales[3] = xs;
+}
+
+static void e4m3_dot(const uint8_t *wrow, const uint8_t *xrow, int64_t k, double folded,
+                     double *y, double *tabs) {
+    double acc = 0.0, aabs = 0.0;
+    for (int64_t i = 0; i < k; i++) {
+        double p = (double)oracle_e4m3_decode(xrow[i]) * (double)oracle_e4m3_decode(wrow[i]);
+        acc += p;
+        aabs += fabs(p);
+    }
+    *y = folded * acc;
+    *tabs = fabs(folded) * aabs;
+}
+
+/*
+ * e4m3 GEMM: y[t][n] = scales[2] * sum_k dec(xq[t][k]) * dec(w[n][k]), fp64.
+ * The fp64 sum of e4m3 products is exact at these sizes.
+ */
+void oracle_e4m3_matmul(const uint8_t *w, const uint8_t *xq, const float *scales,
+                        int64_t m, int64_t k, int64_t n, double *y, double *tabs) {
+    double folded = (double)scales[2];
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t t = 0; t < m; t++)
+            e4m3_dot(w + r * k, xq + t * k, k, folded, &y[t * n + r], &tabs[t * n + r]);
+}
+
+void oracle_e4m3_matmul_sampled(const uint8_t *w, const uint8_t *xq, const float *scales,
+                                int64_t k, int64_t npairs, const int64_t *tok,
+                                const int64_t *row, double *y, double *tabs) {
+    double folded = (double)scales[2];
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npairs; p++)
+        e4m3_dot(w + row[p] * k, xq + tok[p] * k, k, folded, &y[p], &tabs[p]);
+}
