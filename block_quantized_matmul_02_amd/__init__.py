@@ -1,0 +1,167 @@
+"""Python binding of libbqmm, the gfx950 block-quantized projection matmul.
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libbqmm.so`` (built in-tree by ``block_quantized_matmul_02_amd.build``).
+The functions carry the C ABI's names (``include/bqmm.h``), take torch
+tensors that live on the GPU, enqueue on torch's current stream and never
+synchronize.  There is no CPU fallback: a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libbqmm.so")
+
+BQM_OK = 0
+BQM_EINVAL = 1
+BQM_EUNSUPPORTED = 2
+BQM_EHIP_BASE = 10000
+GEMV_MAX_M = 15
+
+_lib = None
+
+
+class BqmError(RuntimeError):
+    def __init__(self, fn: str, rc: int):
+        self.rc = rc
+        super().__init__(f"{fn} failed: rc={rc} ({strerror(rc)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_quantized_matmul_02_amd.build` or __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        L.bqm_q8_1_quantize.argtypes = [P, P, P, I, I, P]
+        L.bqm_q8_0_gemv.argtypes = [P, I64, P, P, P, I, I, I, P]
+        L.bqm_q8_0_gemm.argtypes = [P, I64, P, P, P, I, I, I, P]
+        L.bqm_e4m3_quantize_amax.argtypes = [P, P, P, F, I, I, P]
+        L.bqm_e4m3_gemm.argtypes = [P, P, P, P, I, I, I, P]
+        for fn in ("bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax",
+                   "bqm_e4m3_gemm"):
+            getattr(L, fn).restype = ctypes.c_int
+        L.bqm_strerror.argtypes = [I]
+        L.bqm_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(rc: int) -> str:
+    return lib().bqm_strerror(int(rc)).decode()
+
+
+def _stream(t):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(t, dtype, name, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _raise(fn, rc):
+    if rc != BQM_OK:
+        raise BqmError(fn, rc)
+
+
+def bqm_q8_1_quantize(x, xq=None, xds=None):
+    """q8_1 quantization of f32 ``x [m, k]`` -> (int8 ``xq [m, k]``, f32 ``xds [m, k/32, 2]``)."""
+    import torch
+
+    m, k = x.shape
+    _check(x, torch.float32, "x")
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if xds is None:
+        xds = torch.empty((m, k // 32, 2), dtype=torch.float32, device=x.device)
+    _check(xq, torch.int8, "xq", (m, k))
+    _check(xds, torch.float32, "xds", (m, k // 32, 2))
+    _raise("bqm_q8_1_quantize", lib().bqm_q8_1_quantize(_ptr(x), _ptr(xq), _ptr(xds), m, k, _stream(x)))
+    return xq, xds
+
+
+def _q8_0_args(w, xq, xds, y, k, n):
+    import torch
+
+    m = xq.shape[0]
+    _check(w, torch.uint8, "w")
+    if w.dim() != 2 or w.shape[0] != n:
+        raise ValueError(f"w must be [n={n}, row_bytes], got {tuple(w.shape)}")
+    _check(xq, torch.int8, "xq", (m, k))
+    _check(xds, torch.float32, "xds", (m, k // 32, 2))
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _check(y, torch.float32, "y", (m, n))
+    return m, y
+
+
+def bqm_q8_0_gemv(w, xq, xds, y=None):
+    """Q8_0 GEMV, 1 <= m <= 15: ``w [n, row_bytes]`` uint8 Q8_0 rows -> f32 ``y [m, n]``."""
+    n = w.shape[0]
+    k = xq.shape[1]
+    m, y = _q8_0_args(w, xq, xds, y, k, n)
+    rc = lib().bqm_q8_0_gemv(_ptr(w), w.shape[1], _ptr(xq), _ptr(xds), _ptr(y), m, k, n, _stream(w))
+    _raise("bqm_q8_0_gemv", rc)
+    return y
+
+
+def bqm_q8_0_gemm(w, xq, xds, y=None):
+    """Q8_0 MMQ GEMM, any m: ``w [n, row_bytes]`` uint8 Q8_0 rows -> f32 ``y [m, n]``."""
+    n = w.shape[0]
+    k = xq.shape[1]
+    m, y = _q8_0_args(w, xq, xds, y, k, n)
+    rc = lib().bqm_q8_0_gemm(_ptr(w), w.shape[1], _ptr(xq), _ptr(xds), _ptr(y), m, k, n, _stream(w))
+    _raise("bqm_q8_0_gemm", rc)
+    return y
+
+
+def bqm_e4m3_quantize_amax(x, w_scale: float, xq=None, scales=None):
+    """Per-batch e4m3 quantization of f32 ``x [m, k]`` -> (uint8 codes ``[m, k]``, f32 ``scales[4]``)."""
+    import torch
+
+    m, k = x.shape
+    _check(x, torch.float32, "x")
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(4, dtype=torch.float32, device=x.device)
+    _check(xq, torch.uint8, "xq", (m, k))
+    _check(scales, torch.float32, "scales", (4,))
+    rc = lib().bqm_e4m3_quantize_amax(_ptr(x), _ptr(xq), _ptr(scales), ctypes.c_float(w_scale), m, k, _stream(x))
+    _raise("bqm_e4m3_quantize_amax", rc)
+    return xq, scales
+
+
+def bqm_e4m3_gemm(w, xq, scales, y=None):
+    """e4m3 GEMM: codes ``w [n, k]`` and ``xq [m, k]`` -> f32 ``y [m, n]`` scaled by ``scales[2]``."""
+    import torch
+
+    n, k = w.shape
+    m = xq.shape[0]
+    _check(w, torch.uint8, "w")
+    _check(xq, torch.uint8, "xq", (m, k))
+    _check(scales, torch.float32, "scales", (4,))
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _check(y, torch.float32, "y", (m, n))
+    rc = lib().bqm_e4m3_gemm(_ptr(w), _ptr(xq), _ptr(scales), _ptr(y), m, k, n, _stream(w))
+    _raise("bqm_e4m3_gemm", rc)
+    return y

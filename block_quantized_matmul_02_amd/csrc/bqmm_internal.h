@@ -1,0 +1,61 @@
+// Internal helpers shared by the gfx950 kernels of libbqmm.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bqmm.h"
+
+namespace bqm {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQK = 32;          // values per quantization block
+constexpr int kQ80Bytes = 34;    // Q8_0 block: fp16 scale + 32 int8
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Map the last launch status to the library's return code.
+inline int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? BQM_OK : BQM_EHIP_BASE + (int)e;
+}
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------- device side
+
+// IEEE binary16 bits -> f32 (exact; hardware conversion handles subnormals).
+__device__ __forceinline__ float half_bits_to_float(unsigned h) {
+    _Float16 v = __builtin_bit_cast(_Float16, (unsigned short)(h & 0xFFFFu));
+    return (float)v;
+}
+
+// Butterfly sums inside a row of 16 lanes using DPP; every lane of the row ends
+// with the same value.  Steps: pair lanes (xor 1), quads (xor 2), the two
+// halves of each 8-lane group (half mirror), the two halves of the row (mirror).
+__device__ __forceinline__ float dpp_sum16(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
+// Sum across the 32-lane halves' two rows (lanes r and r^16 within each half).
+__device__ __forceinline__ float swap16_sum(float v) {
+    auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
+    return __builtin_bit_cast(float, s[0]) + __builtin_bit_cast(float, s[1]);
+}
+
+// Sum across the two 32-lane halves of the wave (lanes l and l^32).
+__device__ __forceinline__ float swap32_sum(float v) {
+    auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
+    return __builtin_bit_cast(float, s[0]) + __builtin_bit_cast(float, s[1]);
+}
+
+}  // namespace bqm

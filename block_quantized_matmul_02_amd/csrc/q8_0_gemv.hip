@@ -1,0 +1,327 @@
+// Q8_0 x q8_1 decode/verify GEMV for gfx950 (m = 1..15).
+//
+// What it computes (memra-engine pages): y[t][r] = sum_b d_w[r][b] * d_x[t][b]
+// * S[t][r][b], S the int32 dot product of a 32-block of int8 weight quants
+// with the matching int8 activation quants ("accprobe_bench.rs" module doc:
+// s32 per k32 folded by the two scales; "decode_kernel_census.rs", fn q8: the
+// m=1 Q8_0 GEMV over rows of in_f/32*34 bytes).
+//
+// Design (HBM-bound: every weight byte is read exactly once):
+//  * A weight row is P = K/64 "pairs" of blocks; a pair is 68 bytes = 17
+//    dwords, so pairs are 4-byte aligned while single blocks are not.
+//    Each row is handled by L lanes (L = next power of two >= P, at most
+//    64); lane i of the row owns pairs i, i+L, ...  A wave covers G = 64/L
+//    rows per row-step.
+//  * A wave streams a tile of RT whole rows (<= 16 KiB) with 16-byte buffer
+//    loads: slot s of lane l loads chunk 64*s + l of the tile, so every load
+//    instruction reads 1 KiB of consecutive bytes.  Buffer loads check the
+//    range in hardware: rows past n and unused slots read zeros, never fault.
+//    Two tiles are in flight per wave (register double buffer).
+//  * The tile is written unchanged into a wave-private LDS buffer and read
+//    back pair by pair (17 x ds_read_b32, stride 17 dwords: conflict-free);
+//    the even block's quants sit at a 2-byte offset and are realigned with
+//    v_alignbit (8 ops per pair).
+//  * Activations (int8 quants and d_x) are staged once per workgroup in LDS,
+//    with each pair's four 16-byte chunks rotated by (pair/2) so that eight
+//    lanes reading eight consecutive pairs hit distinct banks.
+//  * Per pair and token: 16 v_dot4_i32_i8, then the two block sums are folded
+//    with fma(float(S), d_w*d_x, acc).  The L per-lane partial sums of a row
+//    are combined by a fixed DPP / permlane-swap butterfly.
+//  * Every token's operation order is the same for any m, so an m-token call
+//    reproduces single-token calls bit for bit ("decode_kernel_census.rs"
+//    module doc: identical per-row FP order across decode and verify).
+#include "bqmm_internal.h"
+
+namespace bqm {
+
+constexpr int kGemvThreads = 256;      // 4 waves, each streaming its own tiles
+constexpr int kGemvWaves = kGemvThreads / 64;
+constexpr int kSlots = 16;             // 16 x 1 KiB per tile
+constexpr int kTileBytes = kSlots * 1024;
+constexpr int kMaxPairsPerSeg = 240;   // 240 * 68 = 16320 bytes <= one tile
+constexpr int kActLdsMax = 98304;      // activation bytes staged per workgroup
+
+struct GemvGeom {
+    int P;         // pairs per row
+    int PS;        // pairs per segment (divides P, multiple of 4)
+    int nseg;      // segments per row
+    int L;         // lanes per row
+    int Llog2;
+    int J;         // pair slots per lane per row-step = ceil(PS / L)
+    int G;         // rows per row-step = 64 / L
+    int RT;        // rows per tile
+    int RS;        // row-steps per tile = RT / G
+    int CPS;       // 16-byte chunks per row segment = 68*PS/16
+    int TC;        // chunks per tile = RT * CPS
+    int n_row_tiles;
+};
+
+// Buffer resource for raw 16-byte loads from [base, base + bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+template <int M>
+__global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
+    const uint8_t *__restrict__ w, int64_t w_row_bytes, const int8_t *__restrict__ xq,
+    const float *__restrict__ xds, float *__restrict__ y, int k, int n, GemvGeom g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int nb = k / kQK;
+    uint8_t *act_q = lds;                                  // [M][k] swizzled per pair
+    float *act_d = reinterpret_cast<float *>(lds + M * k);  // [M][nb]
+    const int act_bytes = (M * k + M * nb * 4 + 15) & ~15;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    uint8_t *tile = lds + act_bytes + wave * kTileBytes;
+
+    // ---- stage activations (once per workgroup)
+    {
+        const int chunks = M * k / 16;
+        for (int c = threadIdx.x; c < chunks; c += kGemvThreads) {
+            int t = c / (k / 16);
+            int cc = c - t * (k / 16);
+            int p = cc >> 2, ci = cc & 3;
+            u32x4 v = *reinterpret_cast<const u32x4 *>(xq + (int64_t)t * k + 16 * cc);
+            int dst = t * k + 64 * p + 16 * ((ci + (p >> 1)) & 3);
+            *reinterpret_cast<u32x4 *>(act_q + dst) = v;
+        }
+        for (int c = threadIdx.x; c < M * nb; c += kGemvThreads) act_d[c] = xds[2 * c];
+    }
+    __syncthreads();
+
+    const int nwaves = gridDim.x * kGemvWaves;
+    const int wid = blockIdx.x * kGemvWaves + wave;
+    if (wid >= g.n_row_tiles) return;
+    const int my_tiles = (g.n_row_tiles - 1 - wid) / nwaves + 1;
+    const int Q = my_tiles * g.nseg;   // work items of this wave: (row tile, segment)
+
+    // Per-slot byte offset of this lane's chunk inside a tile (fixed for all tiles).
+    uint32_t voff[kSlots];
+#pragma unroll
+    for (int s = 0; s < kSlots; s++) {
+        int c = 64 * s + lane;
+        if (c < g.TC) {
+            int r = c / g.CPS;
+            int col = c - r * g.CPS;
+            voff[s] = (uint32_t)(r * w_row_bytes + 16 * col);
+        } else {
+            voff[s] = 0xFFFFFFF0u;   // past num_records: the load returns zeros
+        }
+    }
+
+    auto issue = [&](u32x4 (&buf)[kSlots], int q) {
+        int rt = wid + nwaves * (q / g.nseg);
+        int sg = q - (q / g.nseg) * g.nseg;
+        int64_t row0 = (int64_t)rt * g.RT;
+        const uint8_t *base = w + row0 * w_row_bytes + (int64_t)sg * g.PS * 68;
+        int64_t rem = (int64_t)(n - row0) * w_row_bytes - (int64_t)sg * g.PS * 68;
+        uint32_t bytes = rem > 0x7FFFFFF0ll ? 0x7FFFFFF0u : (uint32_t)rem;
+        __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+#pragma unroll
+        for (int s = 0; s < kSlots; s++) buf[s] = buf_load16(rs, voff[s]);
+    };
+
+    auto stage = [&](const u32x4 (&buf)[kSlots]) {
+        // Wave-private buffer; LDS accesses of one wave complete in order, so the
+        // previous tile's reads are done before these writes land.
+#pragma unroll
+        for (int s = 0; s < kSlots; s++)
+            *reinterpret_cast<u32x4 *>(tile + 1024 * s + 16 * lane) = buf[s];
+    };
+
+    const int li = lane & (g.L - 1);     // lane index inside its row
+    const int gr = lane >> g.Llog2;      // row inside the row-step
+    float acc[M];
+#pragma unroll
+    for (int t = 0; t < M; t++) acc[t] = 0.0f;
+
+    auto compute = [&](int q) {
+        int rt = wid + nwaves * (q / g.nseg);
+        int sg = q - (q / g.nseg) * g.nseg;
+        int row0 = rt * g.RT;
+        for (int rs = 0; rs < g.RS; rs++) {
+            int rl = rs * g.G + gr;
+            if (sg == 0) {
+#pragma unroll
+                for (int t = 0; t < M; t++) acc[t] = 0.0f;
+            }
+            for (int j = 0; j < g.J; j++) {
+                int pl = li + g.L * j;
+                if (pl < g.PS) {
+                    const uint32_t *pw = reinterpret_cast<const uint32_t *>(tile + rl * (68 * g.PS) + 68 * pl);
+                    uint32_t dw[17];
+#pragma unroll
+                    for (int d = 0; d < 17; d++) dw[d] = pw[d];
+                    int qa[8], qb[8];
+#pragma unroll
+                    for (int d = 0; d < 8; d++) {
+                        qa[d] = (int)__builtin_amdgcn_alignbit(dw[d + 1], dw[d], 16u);
+                        qb[d] = (int)dw[9 + d];
+                    }
+                    float da = half_bits_to_float(dw[0]);
+                    float db = half_bits_to_float(dw[8] >> 16);
+                    int p = sg * g.PS + pl;   // pair index in the row
+                    int rot = (p >> 1) & 3;
+#pragma unroll
+                    for (int t = 0; t < M; t++) {
+                        const uint8_t *ap = act_q + t * k + 64 * p;
+                        v4i x0 = *reinterpret_cast<const v4i *>(ap + 16 * ((0 + rot) & 3));
+                        v4i x1 = *reinterpret_cast<const v4i *>(ap + 16 * ((1 + rot) & 3));
+                        v4i x2 = *reinterpret_cast<const v4i *>(ap + 16 * ((2 + rot) & 3));
+                        v4i x3 = *reinterpret_cast<const v4i *>(ap + 16 * ((3 + rot) & 3));
+                        float2 dx = *reinterpret_cast<const float2 *>(act_d + t * nb + 2 * p);
+                        int sa = 0, sb = 0;
+                        sa = __builtin_amdgcn_sdot4(qa[0], x0[0], sa, false);
+                        sa = __builtin_amdgcn_sdot4(qa[1], x0[1], sa, false);
+                        sa = __builtin_amdgcn_sdot4(qa[2], x0[2], sa, false);
+                        sa = __builtin_amdgcn_sdot4(qa[3], x0[3], sa, false);
+                        sa = __builtin_amdgcn_sdot4(qa[4], x1[0], sa, false);
+                        sa = __builtin_amdgcn_sdot4(qa[5], x1[1], sa, false);
+                        sa = __builtin_amdgcn_sdot4(qa[6], x1[2], sa, false);
+                        sa = __builtin_amdgcn_sdot4(qa[7], x1[3], sa, false);
+                        sb = __builtin_amdgcn_sdot4(qb[0], x2[0], sb, false);
+                        sb = __builtin_amdgcn_sdot4(qb[1], x2[1], sb, false);
+                        sb = __builtin_amdgcn_sdot4(qb[2], x2[2], sb, false);
+                        sb = __builtin_amdgcn_sdot4(qb[3], x2[3], sb, false);
+                        sb = __builtin_amdgcn_sdot4(qb[4], x3[0], sb, false);
+                        sb = __builtin_amdgcn_sdot4(qb[5], x3[1], sb, false);
+                        sb = __builtin_amdgcn_sdot4(qb[6], x3[2], sb, false);
+                        sb = __builtin_amdgcn_sdot4(qb[7], x3[3], sb, false);
+                        float sca = da * dx.x;
+                        float scb = db * dx.y;
+                        acc[t] = __builtin_fmaf((float)sa, sca, acc[t]);
+                        acc[t] = __builtin_fmaf((float)sb, scb, acc[t]);
+                    }
+                }
+            }
+            if (sg == g.nseg - 1) {
+                int row = row0 + rl;
+#pragma unroll
+                for (int t = 0; t < M; t++) {
+                    float v = acc[t];
+                    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+                    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+                    if (g.L >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+                    if (g.L >= 16) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+                    if (g.L >= 32) v = swap16_sum(v);
+                    if (g.L >= 64) v = swap32_sum(v);
+                    if (li == 0 && row < n) y[(int64_t)t * n + row] = v;
+                }
+            }
+        }
+    };
+
+    u32x4 bufA[kSlots], bufB[kSlots];
+    issue(bufA, 0);
+    if (Q > 1) issue(bufB, 1);
+    for (int q = 0; q < Q; q += 2) {
+        stage(bufA);
+        if (q + 2 < Q) issue(bufA, q + 2);
+        compute(q);
+        if (q + 1 < Q) {
+            stage(bufB);
+            if (q + 3 < Q) issue(bufB, q + 3);
+            compute(q + 1);
+        }
+    }
+}
+
+static bool make_geom(int k, int n, int64_t w_row_bytes, GemvGeom &g) {
+    g.P = k / 64;
+    g.PS = g.P;
+    if (g.P > kMaxPairsPerSeg) {
+        g.PS = 4;
+        for (int d = kMaxPairsPerSeg; d >= 4; d -= 4)
+            if (g.P % d == 0) { g.PS = d; break; }
+    }
+    g.nseg = g.P / g.PS;
+    int L = 4;
+    while (L < g.P && L < 64) L *= 2;
+    g.L = L;
+    g.Llog2 = __builtin_ctz(L);
+    g.J = (g.PS + L - 1) / L;
+    g.G = 64 / L;
+    int seg_bytes = 68 * g.PS;
+    g.CPS = seg_bytes / 16;
+    if (g.nseg > 1) {
+        g.RT = 1;   // accumulators of one row persist across the segments
+    } else {
+        int steps = kTileBytes / (g.G * seg_bytes);
+        if (steps < 1) return false;
+        if (steps > 8) steps = 8;
+        g.RT = g.G * steps;
+    }
+    g.RS = g.RT / g.G;
+    g.TC = g.RT * g.CPS;
+    if (g.TC > kSlots * 64) return false;
+    g.n_row_tiles = (n + g.RT - 1) / g.RT;
+    (void)w_row_bytes;
+    return true;
+}
+
+template <int M>
+static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y,
+                       int k, int n, const GemvGeom &g, hipStream_t stream) {
+    const int nb = k / kQK;
+    const int act_bytes = (M * k + M * nb * 4 + 15) & ~15;
+    const int lds_bytes = act_bytes + kGemvWaves * kTileBytes;
+    static int attr_done = 0;
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
+        attr_done = 1;
+    }
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int per_cu = (160 * 1024) / lds_bytes;
+    if (per_cu < 1) per_cu = 1;
+    if (per_cu > 4) per_cu = 4;
+    int want = (g.n_row_tiles + kGemvWaves - 1) / kGemvWaves;
+    int grid = cus * per_cu;
+    if (want < grid) grid = want;
+    hipLaunchKernelGGL(q8_0_gemv_kernel<M>, dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w, w_row_bytes, xq,
+                       xds, y, k, n, g);
+    return launch_status();
+}
+
+}  // namespace bqm
+
+extern "C" int bqm_q8_0_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y,
+                             int m, int k, int n, void *stream) {
+    using namespace bqm;
+    if (!w || !xq || !xds || !y) return BQM_EINVAL;
+    if (m < 1 || m > BQM_GEMV_MAX_M || k < 256 || n < 1) return BQM_EINVAL;
+    if (k % 256 != 0) return BQM_EUNSUPPORTED;
+    if (w_row_bytes < (int64_t)(k / kQK) * kQ80Bytes || w_row_bytes % 16 != 0) return BQM_EUNSUPPORTED;
+    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xds, 8) || !aligned(y, 4)) return BQM_EUNSUPPORTED;
+    if ((int64_t)m * k * 9 / 8 > kActLdsMax) return BQM_EUNSUPPORTED;
+    if (w_row_bytes > 0x7FFFFFFF / 64) return BQM_EUNSUPPORTED;
+    GemvGeom g;
+    if (!make_geom(k, n, w_row_bytes, g)) return BQM_EUNSUPPORTED;
+    // the per-slot offsets r*w_row_bytes + 16*col must fit in 32 bits
+    if ((int64_t)g.RT * w_row_bytes > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
+    hipStream_t s = as_stream(stream);
+    switch (m) {
+        case 1: return launch_gemv<1>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 2: return launch_gemv<2>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 3: return launch_gemv<3>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 4: return launch_gemv<4>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 5: return launch_gemv<5>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 6: return launch_gemv<6>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 7: return launch_gemv<7>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 8: return launch_gemv<8>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 9: return launch_gemv<9>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 10: return launch_gemv<10>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 11: return launch_gemv<11>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 12: return launch_gemv<12>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 13: return launch_gemv<13>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 14: return launch_gemv<14>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 15: return launch_gemv<15>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        default: return BQM_EINVAL;
+    }
+}

@@ -1,0 +1,146 @@
+/*
+ * bqmm.h -- C ABI of the block-quantized projection matmul library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * y[m][n] = x[m][k] . W[n][k]^T, the projection matmul of an LLM inference
+ * engine, with two weight encodings:
+ *   - Q8_0 weights (34-byte blocks: fp16 scale + 32 int8 quants) against
+ *     q8_1 activations (int8 + f32 scale per 32 values): each 32-block dot
+ *     product is summed in int32 and folded into f32 by the two scales;
+ *   - OCP E4M3FN weights with one per-tensor f32 scale against activations
+ *     quantized to e4m3 with one per-batch scale amax/448, f32 accumulate.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is DEVICE memory owned by the caller; the
+ *     library allocates nothing, keeps no pointer after returning, and
+ *     never synchronizes the host.  All work is enqueued on `stream`
+ *     (a hipStream_t; NULL means the default stream), in argument order.
+ *   - Output buffers are fully overwritten; they may hold garbage on entry.
+ *   - Matrices are row-major and dense, except Q8_0 weight rows, which
+ *     start every `w_row_bytes` bytes (padding after k/32*34 bytes is
+ *     ignored).
+ *   - Return codes: BQM_OK; BQM_EINVAL for a null pointer or a size out of
+ *     range; BQM_EUNSUPPORTED for a shape or alignment the kernels do not
+ *     handle; BQM_EHIP_BASE + hipError_t when a launch fails.  Argument
+ *     checks run before any HIP call, so a rejected call touches neither
+ *     the device nor the stream.  A launch error is read with
+ *     hipGetLastError(), so an error left pending by the caller's own
+ *     earlier HIP calls is reported here too.
+ *   - Calls on one stream run in order; calls on different streams that
+ *     write the same buffer race (the library has no internal state).
+ *
+ * Passages cited are from the memra-engine docs.rs source pages.
+ */
+#ifndef BQMM_H
+#define BQMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BQM_OK 0
+#define BQM_EINVAL 1
+#define BQM_EUNSUPPORTED 2
+#define BQM_EHIP_BASE 10000
+
+/* Largest token count the GEMV takes ("decode_kernel_census.rs" and
+ * "fp8_ffi.rs" module doc: decode and the m<=9 verify tier stay on the GEMV;
+ * prefill m>=16 moves to the GEMM). */
+#define BQM_GEMV_MAX_M 15
+
+/*
+ * q8_1 activation quantization, per token and 32-value block
+ * ("decode_kernel_census.rs", fn q8: one int8 per column plus a pair of f32
+ * per 32-block; the int8 rule d = amax/127, q = clamp(round(x/d), -127, 127)
+ * with round half away from zero follows "f16_ffi.rs", fn try_f16_gemm,
+ * W8A8 arm; "accprobe_bench.rs" module doc: +-127 at every block amax).
+ *
+ *   x   : f32 [m][k], 16-byte aligned.
+ *   xq  : int8 [m][k] out, 4-byte aligned.
+ *   xds : f32 [m][k/32][2] out, 8-byte aligned: (d, s) with d = amax/127
+ *         (f32 division) and s = d * sum(q) (the pair's second value; the
+ *         Q8_0 kernels never read it).  A block of zeros gives d = s = 0.
+ *   m >= 1, k >= 32, k % 32 == 0 (else BQM_EUNSUPPORTED).
+ * Bytes are identical to a correctly rounded f32 evaluation of the rule.
+ */
+int bqm_q8_1_quantize(const float *x, int8_t *xq, float *xds, int m, int k, void *stream);
+
+/*
+ * Q8_0 decode/verify GEMV, 1 <= m <= 15
+ * ("decode_kernel_census.rs", fn q8: Q8_0 rows of in_f/32*34 bytes timed at
+ * m=1; "fp8_ffi.rs" module doc: m<16 stays on this chain bit for bit and the
+ * verify tier is m<=9).
+ *
+ *   w           : uint8 Q8_0 rows [n][w_row_bytes]; block b of row r is at
+ *                 w + r*w_row_bytes + 34*b (fp16 little-endian d_w, then 32
+ *                 int8 quants).  16-byte aligned.
+ *   w_row_bytes : >= k/32*34 and a multiple of 16.
+ *   xq, xds     : q8_1 activations as written by bqm_q8_1_quantize
+ *                 (xq 16-byte aligned, xds 8-byte aligned).
+ *   y           : f32 [m][n] out, 4-byte aligned.
+ *   k % 256 == 0 (16-byte aligned row segments), and the activations must
+ *   fit on chip: m*k*9/8 <= 98304 bytes (else BQM_EUNSUPPORTED).
+ * y[t][r] = sum_b d_w[r][b] * d_x[t][b] * S[t][r][b], S the int32 block sum;
+ * each token's floating-point operation order does not depend on m, so a
+ * row of an m-token call is bitwise equal to the same row computed alone
+ * ("decode_kernel_census.rs" module doc: identical per-row FP order).
+ */
+int bqm_q8_0_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds,
+                  float *y, int m, int k, int n, void *stream);
+
+/*
+ * Q8_0 prefill GEMM (MMQ), any m >= 1, built for m >= 16
+ * ("accprobe_bench.rs" module doc: int8 MMA with an s32 accumulator per
+ * k32 block folded every k32; "fp8_ffi.rs" module doc: the m>=16 arms).
+ * Same arguments, layouts, result and alignment rules as bqm_q8_0_gemv,
+ * with no limit on m or on k beyond k % 256 == 0.
+ */
+int bqm_q8_0_gemm(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds,
+                  float *y, int m, int k, int n, void *stream);
+
+/*
+ * Per-batch e4m3 activation quantization ("fp8_ffi.rs" module doc: f32 ->
+ * e4m3 with one per-batch scalar scale amax/448, device amax reduce, the
+ * scale folded with weight_scale into a device scalar, no host sync;
+ * Fp8Scratch doc: scale block [0]=amax, [1]=quant mul, [2]=folded scale).
+ *
+ *   x       : f32 [m][k], 16-byte aligned.
+ *   xq      : uint8 [m][k] OCP E4M3FN codes out, 4-byte aligned.
+ *   scales  : f32 [4] out, device memory, 4-byte aligned:
+ *             [0] amax = max|x| over all m*k values,
+ *             [1] mul = 448/amax, [2] folded = (amax/448) * w_scale,
+ *             [3] amax/448; all four are 0 when amax == 0.
+ *   w_scale : the weight tensor's per-tensor scale, finite (else EINVAL).
+ *   m >= 1, k >= 4, k % 4 == 0 (else BQM_EUNSUPPORTED).
+ * xq = e4m3(clamp(x * mul, -448, 448)), round to nearest even, sign of
+ * zero kept; NaN codes (magnitude 0x7F) are never written.
+ */
+int bqm_e4m3_quantize_amax(const float *x, uint8_t *xq, float *scales, float w_scale, int m,
+                           int k, void *stream);
+
+/*
+ * FP8-E4M3 prefill GEMM ("fp8_ffi.rs" module doc and fn try_fp8_gemm:
+ * y[m,out] = x[m,in] @ (e4m3 W)^T, the act scale and weight_scale folded
+ * into one device scalar read by pointer, f32 accumulate).
+ *
+ *   w      : uint8 E4M3FN codes [n][k], 16-byte aligned.
+ *   xq     : uint8 E4M3FN codes [m][k], 16-byte aligned.
+ *   scales : f32 [4] device; only scales[2] is read, on the device.
+ *   y      : f32 [m][n] out, 4-byte aligned.
+ *   k % 128 == 0 (else BQM_EUNSUPPORTED).  Codes with magnitude 0x7F are
+ *   NaN to the matrix cores; callers must not pass them.
+ * y[t][r] = scales[2] * sum_k dec(xq[t][k]) * dec(w[r][k]).
+ */
+int bqm_e4m3_gemm(const uint8_t *w, const uint8_t *xq, const float *scales, float *y, int m,
+                  int k, int n, void *stream);
+
+/* Text for a return code; never NULL, static storage. */
+const char *bqm_strerror(int rc);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQMM_H */

@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/bqmm.h declares, and rejects bad arguments before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bqmm.h")
+PKG = os.path.join(ROOT, "block_quantized_matmul_02_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import block_quantized_matmul_02_amd as bqm
+
+    if not os.path.exists(bqm.LIB_PATH):
+        from block_quantized_matmul_02_amd import build
+
+        build.build()
+    return bqm.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bqm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls_and_strerror():
+    assert declared_symbols() == sorted([
+        "bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax", "bqm_e4m3_gemm",
+        "bqm_strerror"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_strerror(L):
+    import block_quantized_matmul_02_amd as bqm
+
+    assert bqm.strerror(0) == "ok"
+    assert "invalid" in bqm.strerror(1)
+    assert "unsupported" in bqm.strerror(2)
+    assert "HIP" in bqm.strerror(10001)
+
+
+P = ctypes.c_void_p
+A16 = P(0x100000)        # 16-byte aligned stand-ins; never dereferenced (validation fails first)
+B16 = P(0x200000)
+C16 = P(0x300000)
+D16 = P(0x400000)
+MIS2 = P(0x100002)       # 2-byte aligned only
+NUL = P(0)
+
+
+def test_q8_1_quantize_validation(L):
+    f = L.bqm_q8_1_quantize
+    assert f(NUL, B16, C16, 1, 32, NUL) == 1
+    assert f(A16, NUL, C16, 1, 32, NUL) == 1
+    assert f(A16, B16, NUL, 1, 32, NUL) == 1
+    assert f(A16, B16, C16, 0, 32, NUL) == 1
+    assert f(A16, B16, C16, 1, 16, NUL) == 1
+    assert f(A16, B16, C16, 1, 48, NUL) == 2          # k % 32
+    assert f(MIS2, B16, C16, 1, 32, NUL) == 2         # x alignment
+    assert f(A16, MIS2, C16, 1, 32, NUL) == 2
+    assert f(A16, B16, MIS2, 1, 32, NUL) == 2
+
+
+@pytest.mark.parametrize("fn", ["bqm_q8_0_gemv", "bqm_q8_0_gemm"])
+def test_q8_0_validation(L, fn):
+    f = getattr(L, fn)
+    rb = 4096 // 32 * 34
+    assert f(NUL, rb, B16, C16, D16, 1, 4096, 8, NUL) == 1
+    assert f(A16, rb, NUL, C16, D16, 1, 4096, 8, NUL) == 1
+    assert f(A16, rb, B16, NUL, D16, 1, 4096, 8, NUL) == 1
+    assert f(A16, rb, B16, C16, NUL, 1, 4096, 8, NUL) == 1
+    assert f(A16, rb, B16, C16, D16, 0, 4096, 8, NUL) == 1
+    assert f(A16, rb, B16, C16, D16, 1, 4096, 0, NUL) == 1
+    assert f(A16, rb, B16, C16, D16, 1, 4096 + 32, 8, NUL) == 2     # k % 256
+    assert f(A16, rb - 16, B16, C16, D16, 1, 4096, 8, NUL) == 2     # row shorter than k/32*34
+    assert f(A16, rb + 8, B16, C16, D16, 1, 4096, 8, NUL) == 2      # row bytes % 16
+    assert f(MIS2, rb, B16, C16, D16, 1, 4096, 8, NUL) == 2
+    assert f(A16, rb, MIS2, C16, D16, 1, 4096, 8, NUL) == 2
+    assert f(A16, rb, B16, P(0x300004), D16, 1, 4096, 8, NUL) == 2  # xds 8-byte alignment
+    assert f(A16, rb, B16, C16, P(0x400002), 1, 4096, 8, NUL) == 2
+
+
+def test_gemv_m_range_and_on_chip_limit(L):
+    f = L.bqm_q8_0_gemv
+    assert f(A16, 4352, B16, C16, D16, 16, 4096, 8, NUL) == 1          # m > 15
+    rb = 16384 // 32 * 34
+    assert f(A16, rb, B16, C16, D16, 9, 16384, 8, NUL) == 2            # m*k*9/8 > 96 KiB
+
+
+def test_e4m3_validation(L):
+    q = L.bqm_e4m3_quantize_amax
+    F = ctypes.c_float
+    assert q(NUL, B16, C16, F(1.0), 1, 16, NUL) == 1
+    assert q(A16, NUL, C16, F(1.0), 1, 16, NUL) == 1
+    assert q(A16, B16, NUL, F(1.0), 1, 16, NUL) == 1
+    assert q(A16, B16, C16, F(1.0), 0, 16, NUL) == 1
+    assert q(A16, B16, C16, F(float("nan")), 1, 16, NUL) == 1
+    assert q(A16, B16, C16, F(float("inf")), 1, 16, NUL) == 1
+    assert q(A16, B16, C16, F(1.0), 1, 18, NUL) == 2                   # k % 4
+    assert q(MIS2, B16, C16, F(1.0), 1, 16, NUL) == 2
+    g = L.bqm_e4m3_gemm
+    assert g(NUL, B16, C16, D16, 1, 128, 8, NUL) == 1
+    assert g(A16, B16, C16, D16, 1, 128, 0, NUL) == 1
+    assert g(A16, B16, C16, D16, 1, 192, 8, NUL) == 2                  # k % 128
+    assert g(A16, MIS2, C16, D16, 1, 128, 8, NUL) == 2
+
+
+def test_product_path_never_touches_the_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for fname in files:
+            if fname.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fname)).read()
+                assert not re.search(r"\boracle\b", text), f"{fname} mentions the oracle"
