@@ -1,0 +1,211 @@
+"""Benchmark of the block-quantized projection matmul on one MI355X.
+
+One step is one pass of the hot path over one batch of the decode-head
+workload: the q8_1 quantization of the activation (m=1, K=4096) and the Q8_0
+GEMV against the 4096 -> 64448 head (280 MB of weights).  ``value`` is the
+step's algorithmic bytes (weights + activation quants and scales + output) per
+second.  Inputs are resident in HBM before timing starts; three copies of the
+weights are rotated so every step streams its weights from HBM rather than
+the 256 MB Infinity Cache.
+
+The same JSON line also carries the prefill rows, each timed the same way:
+the m=512 MMQ GEMM (q8_1 quantize + int8 GEMM) at N in {4096, 5152, 20480}
+and the FP8-E4M3 GEMM (amax quantize + fp8 GEMM) at N=20480, with int8/fp8
+TOPS and their fraction of the matrix-core peak; a roofline object for the
+dominant kernel (the GEMV), measured with HIP events on the launch stream;
+and the CPU oracle timed on the host cores on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Q8_0 GEMV GB/s (m=1) + MMQ int8 TOPS (m=512), % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA
+FP8_PEAK_TFLOPS = 5000.0         # dense fp8 MFMA
+ROTATE = 3
+
+
+def q8_0_bytes(m, k, n):
+    """Algorithmic bytes of one Q8_0 matmul: weights + xq + xds + y."""
+    return n * (k // 32) * 34 + m * k + m * (k // 32) * 8 + m * n * 4
+
+
+def timed_loop(torch, stream, steps, fns):
+    """Run ``steps`` passes; ``fns`` is a list of (name, callable).  Returns the
+    total wall time of the passes (events around the whole loop) and the mean
+    event-timed duration of each callable."""
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(steps):
+        for j, (_, fn) in enumerate(fns):
+            ev[s][j][0].record(stream)
+            fn(s)
+            ev[s][j][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per = {name: float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(steps)]))
+           for j, (name, _) in enumerate(fns)}
+    return total_ms, per
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3"], default=None,
+                    help="run one part only (for profiler passes)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              "(the path shards along N with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_quantized_matmul_02_amd as bqm
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rng = np.random.default_rng(0)
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+           "data": "synthetic"}
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- decode head GEMV
+    if args.only in (None, "gemv"):
+        m, k, n = 1, 4096, 64448
+        log(f"[bench] generating head weights {n}x{k} Q8_0")
+        w_host = workloads.q8_0_weights(n, k, rng)
+        x_host = workloads.activations(m, k, rng)
+        ws = [torch.from_numpy(w_host).to(dev)]
+        for _ in range(ROTATE - 1):
+            ws.append(ws[0].clone())
+        x = torch.from_numpy(x_host).to(dev)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        xds = torch.empty((m, k // 32, 2), dtype=torch.float32, device=dev)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        fns = [("quantize", lambda s: bqm.bqm_q8_1_quantize(x, xq, xds)),
+               ("gemv", lambda s: bqm.bqm_q8_0_gemv(ws[s % ROTATE], xq, xds, y))]
+        log("[bench] gemv warmup")
+        timed_loop(torch, stream, args.warmup, fns)
+        log("[bench] gemv timed")
+        total_ms, per = timed_loop(torch, stream, args.steps, fns)
+        step_bytes = q8_0_bytes(m, k, n) + m * k * 4 + m * k + m * (k // 32) * 8   # + quantize pass
+        ms_step = total_ms / args.steps
+        gemv_bytes = q8_0_bytes(m, k, n)
+        achieved = gemv_bytes / (per["gemv"] * 1e-3) / 1e9
+        out.update({
+            "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+            "unit": "GB/s",
+            "ms_per_step": round(ms_step, 5),
+            "config": {"workload": "decode head GEMV: m=1, K=4096, N=64448, Q8_0 weights, q8_1 activations",
+                       "m": m, "k": k, "n": n, "weight_copies_rotated": ROTATE, "parallelism": "none"},
+            "roofline": {"bound": "hbm", "kernel": "q8_0_gemv_kernel<1>", "achieved": round(achieved, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": None, "bytes_per_launch": gemv_bytes,
+                         "avg_launch_us": round(per["gemv"] * 1e3, 3)},
+            "steps_detail_us": {k2: round(v * 1e3, 3) for k2, v in per.items()},
+        })
+        del ws
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- prefill MMQ
+    if args.only in (None, "mmq"):
+        mmq = {}
+        m, k = 512, 4096
+        x_host = workloads.activations(m, k, rng, outliers=True)
+        x = torch.from_numpy(x_host).to(dev)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        xds = torch.empty((m, k // 32, 2), dtype=torch.float32, device=dev)
+        for n in workloads.GEMM_NS:
+            log(f"[bench] mmq n={n}")
+            w0 = torch.from_numpy(workloads.q8_0_weights(n, k, rng)).to(dev)
+            ws = [w0] + [w0.clone() for _ in range(ROTATE - 1)]
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            fns = [("quantize", lambda s: bqm.bqm_q8_1_quantize(x, xq, xds)),
+                   ("gemm", lambda s: bqm.bqm_q8_0_gemm(ws[s % ROTATE], xq, xds, y))]
+            timed_loop(torch, stream, args.warmup, fns)
+            total_ms, per = timed_loop(torch, stream, args.steps, fns)
+            ops = 2.0 * m * n * k
+            tops = ops / (per["gemm"] * 1e-3) / 1e12
+            mmq[str(n)] = {"workload": f"MMQ GEMM m=512, K=4096, N={n}, Q8_0 x q8_1 (1% outliers x10)",
+                           "gemm_us": round(per["gemm"] * 1e3, 2), "quantize_us": round(per["quantize"] * 1e3, 2),
+                           "tops": round(tops, 1), "unit": "TOPS",
+                           "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+                           "step_tops": round(ops / (total_ms / args.steps * 1e-3) / 1e12, 1)}
+            del ws, w0, y
+            torch.cuda.empty_cache()
+        out["mmq_m512"] = mmq
+
+    # ---------------------------------------------------------------- FP8 prefill
+    if args.only in (None, "e4m3"):
+        m, k, n = 512, 4096, 20480
+        log("[bench] e4m3 n=20480")
+        codes, w_scale = workloads.e4m3_weights(n, k, rng)
+        w0 = torch.from_numpy(codes).to(dev)
+        ws = [w0] + [w0.clone() for _ in range(ROTATE - 1)]
+        x = torch.from_numpy(workloads.activations(m, k, rng)).to(dev)
+        xq8 = torch.empty((m, k), dtype=torch.uint8, device=dev)
+        sc = torch.empty(4, dtype=torch.float32, device=dev)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        fns = [("quantize", lambda s: bqm.bqm_e4m3_quantize_amax(x, w_scale, xq8, sc)),
+               ("gemm", lambda s: bqm.bqm_e4m3_gemm(ws[s % ROTATE], xq8, sc, y))]
+        timed_loop(torch, stream, args.warmup, fns)
+        total_ms, per = timed_loop(torch, stream, args.steps, fns)
+        ops = 2.0 * m * n * k
+        tf = ops / (per["gemm"] * 1e-3) / 1e12
+        out["e4m3_m512"] = {"workload": "FP8-E4M3 GEMM m=512, K=4096, N=20480, per-batch amax/448",
+                            "gemm_us": round(per["gemm"] * 1e3, 2), "quantize_us": round(per["quantize"] * 1e3, 2),
+                            "tflops": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+                            "step_tflops": round(ops / (total_ms / args.steps * 1e-3) / 1e12, 1)}
+        del ws, w0, y
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu and args.only in (None, "gemv"):
+        import oracle
+
+        m, k, n = 1, 4096, 64448
+        w_host = workloads.q8_0_weights(n, k, np.random.default_rng(0))
+        x_host = workloads.activations(m, k, np.random.default_rng(1))
+        reps, t_total = 0, 0.0
+        t0 = time.perf_counter()
+        while t_total < 10.0 and reps < 200:
+            xq_h, xds_h = oracle.q8_1_quantize(x_host)
+            oracle.q8_0_matmul(w_host, xq_h, xds_h, k)
+            reps += 1
+            t_total = time.perf_counter() - t0
+        gbs = reps * (q8_0_bytes(m, k, n) + m * k * 4) / t_total / 1e9
+        out["cpu_baseline"] = {"value": round(gbs, 2), "unit": "GB/s", "cores": oracle.num_threads(),
+                               "kind": "oracle",
+                               "sample": f"the full decode-head step (q8_1 quantize + Q8_0 matmul, m=1, "
+                                         f"K=4096, N=64448) repeated {reps} times in {t_total:.1f} s"}
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -46,16 +46,38 @@ __device__ __forceinline__ float dpp_sum16(float v) {
     return v;
 }
 
-// Sum across the 32-lane halves' two rows (lanes r and r^16 within each half).
+// The swap builtins return a 2-vector {new vdst, new src0}.  Each element is
+// copied to a scalar before any bit cast: clang lowers a __builtin_bit_cast of
+// a vector-element expression to a load from the vector's first element.
+// Sum of lanes l and l^16 (rows 0/1 and 2/3 exchanged by v_permlane16_swap).
 __device__ __forceinline__ float swap16_sum(float v) {
-    auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
-    return __builtin_bit_cast(float, s[0]) + __builtin_bit_cast(float, s[1]);
+    unsigned u = __builtin_bit_cast(unsigned, v);
+    auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    unsigned a = s[0], b = s[1];
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
-// Sum across the two 32-lane halves of the wave (lanes l and l^32).
+// Sum of lanes l and l^32 (the wave's halves exchanged by v_permlane32_swap).
 __device__ __forceinline__ float swap32_sum(float v) {
-    auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
-    return __builtin_bit_cast(float, s[0]) + __builtin_bit_cast(float, s[1]);
+    unsigned u = __builtin_bit_cast(unsigned, v);
+    auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    unsigned a = s[0], b = s[1];
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// Max of lanes l, l^16 and of lanes l, l^32.
+__device__ __forceinline__ float swap16_max(float v) {
+    unsigned u = __builtin_bit_cast(unsigned, v);
+    auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    unsigned a = s[0], b = s[1];
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
+__device__ __forceinline__ float swap32_max(float v) {
+    unsigned u = __builtin_bit_cast(unsigned, v);
+    auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    unsigned a = s[0], b = s[1];
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 }  // namespace bqm

@@ -2,7 +2,8 @@
 //
 // Rule per (token, 32-value block), from the memra-engine pages: d = amax/127
 // (f32 division), q = clamp(round_half_away(x/d), -127, 127), and the pair's
-// second value s = d * sum(q) ("decode_kernel_census.rs", fn q8: int8 per
+// second value s = d * sum(q); a block whose d is 0 (amax == 0, or amax/127
+// underflowing) quantizes to zeros ("decode_kernel_census.rs", fn q8: int8 per
 // column plus a per-32 scale pair; "f16_ffi.rs", fn try_f16_gemm, W8A8 arm:
 // the int8 rule with Rust's round).
 //
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(256) void q8_1_quantize_kernel(const float4 *__rest
     float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     float amax = max8(a);
     float d = amax / 127.0f;
-    bool nz = amax > 0.0f;
+    bool nz = d > 0.0f;   // amax == 0, or amax/127 underflowing to 0: an all-zero block
     int q0 = quant1(v.x, d, nz), q1 = quant1(v.y, d, nz), q2 = quant1(v.z, d, nz), q3 = quant1(v.w, d, nz);
     int sum = isum8(q0 + q1 + q2 + q3);
     if (valid) {

@@ -78,9 +78,11 @@ static float round_half_away(float v) {
  *   amax = max |x_i|;  d = amax / 127 (f32 division);
  *   q_i = clamp(round_half_away(x_i / d), -127, 127) (f32 division);
  *   s = d * (float)sum(q_i)  -- the second value of the scale pair.
- * Readings: amax == 0 gives d = 0, q = 0, s = 0 (the W8A8 arm leaves an
- * all-zero row untouched); the second pair value is d times the quant sum
- * (the pages only say "a pair", the Q8_0 path never reads it).
+ * Readings: a block whose d is 0 -- amax == 0, or amax so small (below
+ * 127 * 2^-150) that amax/127 underflows to 0 -- gives q = 0 and s = 0 (the
+ * W8A8 arm leaves an all-zero row untouched; dividing by d = 0 has no int8
+ * meaning); the second pair value is d times the quant sum (the pages only
+ * say "a pair", the Q8_0 path never reads it).
  * xds layout: [m][k/32][2] = (d, s).
  */
 void oracle_q8_1_quantize(const float *x, int8_t *xq, float *xds, int64_t m, int64_t k) {
@@ -98,7 +100,7 @@ void oracle_q8_1_quantize(const float *x, int8_t *xq, float *xds, int64_t m, int
             int sum = 0;
             for (int i = 0; i < QK; i++) {
                 float r = 0.0f;
-                if (amax > 0.0f) {
+                if (d > 0.0f) {
                     r = round_half_away(blk[i] / d);
                     if (r > 127.0f) r = 127.0f;
                     if (r < -127.0f) r = -127.0f;

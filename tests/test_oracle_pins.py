@@ -85,6 +85,19 @@ def test_q8_1_zero_block():
     assert xds[1, 1, 0] > 0
 
 
+def test_q8_1_block_whose_scale_underflows_is_zero():
+    # amax = 2^-149 (the smallest subnormal): amax/127 < 2^-150 rounds to 0 in
+    # f32, so the block is treated like an all-zero block.
+    x = np.zeros((1, 64), dtype=np.float32)
+    x[0, 5] = np.float32(2.0 ** -149)
+    x[0, 6] = -np.float32(0.0)
+    x[0, 32] = np.float32(127 * 2.0 ** -149)     # d = 2^-149 exactly: the smallest non-zero scale
+    xq, xds = oracle.q8_1_quantize(x)
+    assert np.float32(x[0, 5]) / np.float32(127) == 0
+    assert np.all(xq[0, :32] == 0) and np.all(xds[0, 0] == 0)
+    assert xds[0, 1, 0] == np.float32(2.0 ** -149) and xq[0, 32] == 127
+
+
 def test_q8_1_power_of_two_scaling_and_negation_are_exact():
     rng = np.random.default_rng(3)
     x = rng.standard_normal((4, 256)).astype(np.float32)
