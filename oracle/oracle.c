@@ -262,11 +262,18 @@ void oracle_e4m3_quantize_amax(const float *x, uint8_t *xq, float *scales, float
     scales[3] = xs;
 }
 
+/* Decode table for the 256 codes, filled from oracle_e4m3_decode before use. */
+static double e4m3_table[256];
+
+static void e4m3_fill_table(void) {
+    for (int c = 0; c < 256; c++) e4m3_table[c] = (double)oracle_e4m3_decode((uint8_t)c);
+}
+
 static void e4m3_dot(const uint8_t *wrow, const uint8_t *xrow, int64_t k, double folded,
                      double *y, double *tabs) {
     double acc = 0.0, aabs = 0.0;
     for (int64_t i = 0; i < k; i++) {
-        double p = (double)oracle_e4m3_decode(xrow[i]) * (double)oracle_e4m3_decode(wrow[i]);
+        double p = e4m3_table[xrow[i]] * e4m3_table[wrow[i]];
         acc += p;
         aabs += fabs(p);
     }
@@ -281,6 +288,7 @@ static void e4m3_dot(const uint8_t *wrow, const uint8_t *xrow, int64_t k, double
 void oracle_e4m3_matmul(const uint8_t *w, const uint8_t *xq, const float *scales,
                         int64_t m, int64_t k, int64_t n, double *y, double *tabs) {
     double folded = (double)scales[2];
+    e4m3_fill_table();
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < n; r++)
         for (int64_t t = 0; t < m; t++)
@@ -291,6 +299,7 @@ void oracle_e4m3_matmul_sampled(const uint8_t *w, const uint8_t *xq, const float
                                 int64_t k, int64_t npairs, const int64_t *tok,
                                 const int64_t *row, double *y, double *tabs) {
     double folded = (double)scales[2];
+    e4m3_fill_table();
 #pragma omp parallel for schedule(static)
     for (int64_t p = 0; p < npairs; p++)
         e4m3_dot(w + row[p] * k, xq + tok[p] * k, k, folded, &y[p], &tabs[p]);
