@@ -44,22 +44,27 @@ def q8_0_bytes(m, k, n):
 
 
 def timed_loop(torch, stream, steps, fns):
-    """Run ``steps`` passes; ``fns`` is a list of (name, callable).  Returns the
-    total wall time of the passes (events around the whole loop) and the mean
-    event-timed duration of each callable."""
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
-          for _ in range(steps)]
+    """Time ``steps`` passes of ``fns`` (a list of (name, callable)) twice: once
+    with events only around the whole loop (the step time, no gaps added by
+    timing), then with events around every call (each kernel's mean duration on
+    the launch stream).  Returns (total ms of the first loop, {name: mean ms})."""
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
+    for s in range(steps):
+        for _, fn in fns:
+            fn(s)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(steps)]
     for s in range(steps):
         for j, (_, fn) in enumerate(fns):
             ev[s][j][0].record(stream)
             fn(s)
             ev[s][j][1].record(stream)
-    end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
     per = {name: float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(steps)]))
            for j, (name, _) in enumerate(fns)}
     return total_ms, per
@@ -71,8 +76,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3"], default=None,
-                    help="run one part only (for profiler passes)")
+    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3", "copy"], default=None,
+                    help="run one part only (for profiler passes); 'copy' runs a plain 1 GiB device copy "
+                         "that calibrates the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
@@ -93,6 +99,15 @@ def main():
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
+
+    if args.only == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "launches": args.steps}), flush=True)
+        return
 
     # ---------------------------------------------------------------- decode head GEMV
     if args.only in (None, "gemv"):

@@ -40,6 +40,11 @@ constexpr int kSlots = 16;             // 16 x 1 KiB per tile
 constexpr int kTileBytes = kSlots * 1024;
 constexpr int kMaxPairsPerSeg = 240;   // 240 * 68 = 16320 bytes <= one tile
 constexpr int kActLdsMax = 98304;      // activation bytes staged per workgroup
+// Cache policy of the weight loads: non-temporal.  Every weight byte is read
+// exactly once, so keeping it out of the caches frees them for the activations
+// (measured: a plain 280 MB stream reads at 5.75 TB/s with the default policy
+// and 6.5 TB/s non-temporal on MI355X).
+constexpr int kWeightLoadPolicy = 2;
 
 struct GemvGeom {
     int P;         // pairs per row
@@ -62,7 +67,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kWeightLoadPolicy));
 }
 
 template <int M>
@@ -78,8 +83,9 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     const int lane = threadIdx.x & 63;
     uint8_t *tile = lds + act_bytes + wave * kTileBytes;
 
-    // ---- stage activations (once per workgroup)
-    {
+    // Activations (int8 quants and d_x) are staged once per workgroup, after
+    // the first weight tiles are in flight so HBM starts streaming at once.
+    auto stage_activations = [&]() {
         const int chunks = M * k / 16;
         for (int c = threadIdx.x; c < chunks; c += kGemvThreads) {
             int t = c / (k / 16);
@@ -90,13 +96,13 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
             *reinterpret_cast<u32x4 *>(act_q + dst) = v;
         }
         for (int c = threadIdx.x; c < M * nb; c += kGemvThreads) act_d[c] = xds[2 * c];
-    }
-    __syncthreads();
+        __syncthreads();
+    };
 
     const int nwaves = gridDim.x * kGemvWaves;
     const int wid = blockIdx.x * kGemvWaves + wave;
-    if (wid >= g.n_row_tiles) return;
-    const int my_tiles = (g.n_row_tiles - 1 - wid) / nwaves + 1;
+    // Waves without a tile still take part in the workgroup barrier.
+    const int my_tiles = wid < g.n_row_tiles ? (g.n_row_tiles - 1 - wid) / nwaves + 1 : 0;
     const int Q = my_tiles * g.nseg;   // work items of this wave: (row tile, segment)
 
     // Per-slot byte offset of this lane's chunk inside a tile (fixed for all tiles).
@@ -216,8 +222,9 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     };
 
     u32x4 bufA[kSlots], bufB[kSlots];
-    issue(bufA, 0);
+    if (Q > 0) issue(bufA, 0);
     if (Q > 1) issue(bufB, 1);
+    stage_activations();
     for (int q = 0; q < Q; q += 2) {
         stage(bufA);
         if (q + 2 < Q) issue(bufA, q + 2);
