@@ -44,10 +44,14 @@ def q8_0_bytes(m, k, n):
 
 
 def timed_loop(torch, stream, steps, fns):
-    """Time ``steps`` passes of ``fns`` (a list of (name, callable)) twice: once
-    with events only around the whole loop (the step time, no gaps added by
-    timing), then with events around every call (each kernel's mean duration on
-    the launch stream).  Returns (total ms of the first loop, {name: mean ms})."""
+    """Time ``steps`` passes of ``fns`` (a list of (name, callable)).
+
+    The step time comes from events around the whole loop, with nothing added
+    between calls.  Each callable's duration comes from a second loop per
+    callable that launches it ``steps`` times back to back between two events
+    on the launch stream (so per-event overhead is amortized; the inter-launch
+    gap stays in, which errs on the slow side).
+    Returns (total ms of the step loop, {name: mean ms per call})."""
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -57,16 +61,15 @@ def timed_loop(torch, stream, steps, fns):
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
-          for _ in range(steps)]
-    for s in range(steps):
-        for j, (_, fn) in enumerate(fns):
-            ev[s][j][0].record(stream)
+    per = {}
+    for name, fn in fns:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for s in range(steps):
             fn(s)
-            ev[s][j][1].record(stream)
-    torch.cuda.synchronize()
-    per = {name: float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(steps)]))
-           for j, (name, _) in enumerate(fns)}
+        b.record(stream)
+        torch.cuda.synchronize()
+        per[name] = a.elapsed_time(b) / steps
     return total_ms, per
 
 
