@@ -4,7 +4,10 @@ Every HIP source is compiled on its own (in parallel) and linked into one
 shared library next to this file.  Flags:
   -ffp-contract=off   floating-point contraction only where a kernel writes
                       an explicit fma, so results do not depend on inlining;
-  -packed-fp32-ops    removed from the target features: no packed f32 VALU.
+  -packed-fp32-ops    removed from the target features: no packed f32 VALU;
+  -amdgpu-mfma-vgpr-form=1
+                      MFMA sources and results in ordinary VGPRs, so the
+                      VALU fold reads the int32 block sums without copies.
 """
 from __future__ import annotations
 
@@ -31,6 +34,7 @@ HIPFLAGS = [
     "-fPIC",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

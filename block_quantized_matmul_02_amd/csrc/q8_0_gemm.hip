@@ -8,18 +8,31 @@
 //
 // gfx950 mapping:
 //  * v_mfma_i32_32x32x32_i8 has K = 32, exactly one Q8_0 block, so one MFMA
-//    gives S for a 32x32 output tile and one block; its int32 result is
-//    folded at once (cvt, scale product, fma).  The fold runs on the VALU
-//    and bounds the kernel; the matrix cores are idle most of the time.
-//  * Workgroup tile 64 tokens x 64 weight rows, 4 waves of 32x32, K staged
-//    256 values (8 blocks) at a time.  Global loads are coalesced 16-byte
-//    buffer loads (range-checked in hardware: ragged m and n tails read
-//    zeros), prefetched into registers one stage ahead.
-//  * Weight rows arrive in 34-byte blocks whose quants are 2-byte aligned;
-//    the raw bytes are staged in LDS, then realigned with v_alignbit into a
-//    dense quant tile and an f32 scale array.
-//  * Quant tiles use a 16-byte-chunk XOR swizzle (chunk ^ (row & 7)) so the
-//    MFMA operand reads of 8 consecutive rows hit distinct banks.
+//    gives the int32 block sums S of a 32x32 output tile.
+//  * The fold is per output element and block: acc = fma(float(S),
+//    d_x * d_w, acc), three VALU ops.  Without packed f32 the VALU retires a
+//    wave64 op every 4 clk, so the fold (192 clk per 32x32 tile and block)
+//    bounds the kernel and the MFMA (about 37 clk) hides under it; measured on
+//    MI355X, an int8 MFMA plus this fold per block runs at 190 clk.  The
+//    MFMA of block b+1 is issued before the fold of block b, and the LDS
+//    operands are read two blocks ahead, so the matrix core, the LDS and the
+//    VALU overlap.  MFMA results stay in ordinary VGPRs (the build asks for
+//    the VGPR form), so the fold reads them without copies.
+//  * Workgroup tile 64 tokens x 64 weight rows, 4 waves of 32x32; k is staged
+//    256 values (8 blocks) at a time into double-buffered LDS, and the global
+//    loads run two stages ahead in a register double buffer to cover L2 and
+//    Infinity Cache latency (one barrier per stage).
+//  * Weight rows are 34-byte blocks whose quants are 2-byte aligned.  Each
+//    thread loads one 68-byte block pair (4-byte aligned) straight into
+//    registers, realigns the even block with v_alignbit, and writes dense
+//    quants plus f32 scales to LDS.
+//  * Quant tiles are stored with a padded row stride of 272 bytes (256 + 16),
+//    so the MFMA operand reads of 8 consecutive rows at the same k hit
+//    distinct banks and every LDS address is a per-lane base plus a
+//    compile-time offset; the scale reads of the fold are broadcasts (every
+//    lane of a half-wave reads the same four rows).
+//  * Global loads are range-checked buffer loads: ragged m and n tails read
+//    zeros (zero scales), and only in-range outputs are stored.
 #include "bqmm_internal.h"
 
 namespace bqm {
@@ -28,23 +41,35 @@ constexpr int kMmqBM = 64;
 constexpr int kMmqBN = 64;
 constexpr int kMmqKB = 256;                  // k values per stage = 8 blocks
 constexpr int kMmqBlocks = kMmqKB / kQK;     // 8
-constexpr int kMmqRawRow = kMmqBlocks * kQ80Bytes;   // 272 bytes
+constexpr int kMmqPairBytes = 2 * kQ80Bytes; // 68
 constexpr int kMmqThreads = 256;
+constexpr int kMmqRowStride = kMmqKB + 16;   // 272: padded LDS row of quants
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t mmq_rsrc(const void *base, int64_t bytes) {
     uint32_t b = bytes <= 0 ? 0u : (bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0u : (uint32_t)bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)b, 0x00020000);
 }
 
+struct MmqStage {
+    uint8_t x[kMmqBM * kMmqRowStride];   // activation quants, padded rows
+    uint8_t w[kMmqBN * kMmqRowStride];   // weight quants, padded rows
+    float dx[kMmqBlocks][kMmqBM];        // d_x per block and token row
+    float dw[kMmqBlocks][kMmqBN];        // d_w per block and weight row
+};
+
+// Global loads of one stage, held in registers until written to LDS.
+struct MmqRegs {
+    u32x4 x[4];      // 4 activation chunks
+    u32x4 w[4];      // one 68-byte weight block pair: dwords 0..15
+    uint32_t w16;    // and dword 16
+    float dx[2];     // 2 (row, block) activation scales
+};
+
 __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *__restrict__ w, int64_t w_row_bytes,
                                                               const int8_t *__restrict__ xq,
                                                               const float *__restrict__ xds, float *__restrict__ y,
                                                               int m, int k, int n) {
-    __shared__ __attribute__((aligned(16))) uint8_t sX[kMmqBM * kMmqKB];        // swizzled quants
-    __shared__ __attribute__((aligned(16))) uint8_t sW[kMmqBN * kMmqKB];        // swizzled quants
-    __shared__ __attribute__((aligned(16))) uint8_t sWraw[kMmqBN * kMmqRawRow];  // raw 34-byte blocks
-    __shared__ float sDX[kMmqBlocks][kMmqBM];
-    __shared__ float sDW[kMmqBlocks][kMmqBN];
+    __shared__ __attribute__((aligned(16))) MmqStage st[2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -60,49 +85,76 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
     const __amdgpu_buffer_rsrc_t rD = mmq_rsrc(xds + (int64_t)m0 * nb * 2, (int64_t)(m - m0) * nb * 8);
     const __amdgpu_buffer_rsrc_t rW = mmq_rsrc(w + (int64_t)n0 * w_row_bytes, (int64_t)(n - n0) * w_row_bytes);
 
-    // Per-thread load slots.  X: 1024 chunks, 4 per thread.  Wraw: 1088 chunks,
-    // 5 slots (the fifth for tid < 64).  dX: 512 floats, 2 per thread.
-    u32x4 rx[4], rw[5];
-    float rdx[2];
-    auto load_stage = [&](int kc) {
+    // This thread's load slots, as byte offsets fixed for the whole kernel; the
+    // stage offset is a uniform scalar added by the buffer load (soffset).
+    // X: 4 chunks (row q>>4, chunk q&15).  W: one 68-byte block pair (row
+    // tid>>2, pair tid&3).  dX: 2 (row q>>3, block q&7), the d of each pair.
+    const int wrow = tid >> 2, wpair = tid & 3;
+    const uint32_t woff = (uint32_t)(wrow * w_row_bytes + kMmqPairBytes * wpair);
+    uint32_t xoff[4], doff[2];
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-            int q = tid + 256 * s;
-            int row = q >> 4, c = q & 15;
-            uint32_t off = (uint32_t)(row * k + kc * kMmqKB + 16 * c);
-            rx[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0));
-        }
+    for (int s = 0; s < 4; s++) {
+        const int q = tid + 256 * s;
+        xoff[s] = (uint32_t)((q >> 4) * k + 16 * (q & 15));
+    }
 #pragma unroll
-        for (int s = 0; s < 5; s++) {
-            int q = tid + 256 * s;
-            int row = q / 17, c = q - row * 17;
-            uint32_t off = (q < kMmqBN * 17) ? (uint32_t)(row * w_row_bytes + kc * kMmqRawRow + 16 * c) : 0xFFFFFFF0u;
-            rw[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0));
-        }
+    for (int s = 0; s < 2; s++) {
+        const int q = tid + 256 * s;
+        doff[s] = (uint32_t)(((q >> 3) * nb + (q & 7)) * 8);
+    }
+    auto load_stage = [&](MmqRegs &R, int kc) {
+        const int sx = kc * kMmqKB, sw = kc * (kMmqBlocks * kQ80Bytes), sd = kc * kMmqBlocks * 8;
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
-            int q = tid + 256 * s;
-            int row = q >> 3, b = q & 7;
-            uint32_t off = (uint32_t)(((int64_t)row * nb + kc * kMmqBlocks + b) * 8);
-            rdx[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, off, 0, 0));
-        }
+        for (int s = 0; s < 4; s++)
+            R.x[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, xoff[s], sx, 0));
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+            R.w[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, woff + 16 * s, sw, 0));
+        R.w16 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, woff + 64, sw, 0);
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+            R.dx[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, doff[s], sd, 0));
     };
-    auto store_stage = [&]() {
+    auto store_stage = [&](MmqStage &S, const MmqRegs &R) {
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             int q = tid + 256 * s;
             int row = q >> 4, c = q & 15;
-            *reinterpret_cast<u32x4 *>(sX + row * kMmqKB + 16 * (c ^ (row & 7))) = rx[s];
+            *reinterpret_cast<u32x4 *>(S.x + row * kMmqRowStride + 16 * c) = R.x[s];
         }
+        // realign the block pair: the even block's quants start 2 bytes into dword 0
+        uint32_t d[17];
 #pragma unroll
-        for (int s = 0; s < 5; s++) {
-            int q = tid + 256 * s;
-            if (q < kMmqBN * 17) *reinterpret_cast<u32x4 *>(sWraw + 16 * q) = rw[s];
+        for (int s = 0; s < 4; s++) {
+            d[4 * s + 0] = R.w[s][0];
+            d[4 * s + 1] = R.w[s][1];
+            d[4 * s + 2] = R.w[s][2];
+            d[4 * s + 3] = R.w[s][3];
         }
+        d[16] = R.w16;
+        u32x4 qa0, qa1;
+        qa0[0] = __builtin_amdgcn_alignbit(d[1], d[0], 16u);
+        qa0[1] = __builtin_amdgcn_alignbit(d[2], d[1], 16u);
+        qa0[2] = __builtin_amdgcn_alignbit(d[3], d[2], 16u);
+        qa0[3] = __builtin_amdgcn_alignbit(d[4], d[3], 16u);
+        qa1[0] = __builtin_amdgcn_alignbit(d[5], d[4], 16u);
+        qa1[1] = __builtin_amdgcn_alignbit(d[6], d[5], 16u);
+        qa1[2] = __builtin_amdgcn_alignbit(d[7], d[6], 16u);
+        qa1[3] = __builtin_amdgcn_alignbit(d[8], d[7], 16u);
+        const u32x4 qb0 = {d[9], d[10], d[11], d[12]};
+        const u32x4 qb1 = {d[13], d[14], d[15], d[16]};
+        const int b0 = 2 * wpair;
+        uint8_t *wr = S.w + wrow * kMmqRowStride + 32 * b0;
+        *reinterpret_cast<u32x4 *>(wr + 0) = qa0;
+        *reinterpret_cast<u32x4 *>(wr + 16) = qa1;
+        *reinterpret_cast<u32x4 *>(wr + 32) = qb0;
+        *reinterpret_cast<u32x4 *>(wr + 48) = qb1;
+        S.dw[b0][wrow] = half_bits_to_float(d[0]);
+        S.dw[b0 + 1][wrow] = half_bits_to_float(d[8] >> 16);
 #pragma unroll
         for (int s = 0; s < 2; s++) {
             int q = tid + 256 * s;
-            sDX[q & 7][q >> 3] = rdx[s];
+            S.dx[q & 7][q >> 3] = R.dx[s];
         }
     };
 
@@ -114,56 +166,76 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
     const int brow = wn * 32 + (lane & 31);   // B operand row (weight row) of this lane
     const int khalf = lane >> 5;
 
-    load_stage(0);
-    for (int kc = 0; kc < nstage; kc++) {
-        store_stage();
-        __syncthreads();
-        if (kc + 1 < nstage) load_stage(kc + 1);
-        // realign 64 rows x 8 blocks: 2 (row, block) items per thread
+    // One stage: 8 blocks.  Quant operands are read two blocks ahead, the MFMA
+    // and the fold's scales one block ahead, so no LDS or MFMA latency sits in
+    // front of a fold.
+    auto compute_stage = [&](const MmqStage &S) {
+        v4i A[3], B[3];
+        float4 DX[2][4];
+        float DW[2];
+        const uint8_t *xa = S.x + arow * kMmqRowStride + 16 * khalf;
+        const uint8_t *wb = S.w + brow * kMmqRowStride + 16 * khalf;
+        auto rd = [&](int b, int slot) {
+            A[slot] = *reinterpret_cast<const v4i *>(xa + 32 * b);
+            B[slot] = *reinterpret_cast<const v4i *>(wb + 32 * b);
+        };
+        auto rds = [&](int b, int slot) {
+            const float *dxp = &S.dx[b][wm * 32 + 4 * khalf];
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
-            int it = tid + 256 * s;
-            int row = it & 63, b = it >> 6;
-            const uint32_t *rp = reinterpret_cast<const uint32_t *>(sWraw + row * kMmqRawRow + 68 * (b >> 1));
-            uint32_t q[8];
-            uint32_t sbits;
-            if ((b & 1) == 0) {
-                uint32_t dw[9];
+            for (int qd = 0; qd < 4; qd++) DX[slot][qd] = *reinterpret_cast<const float4 *>(dxp + 8 * qd);
+            DW[slot] = S.dw[b][brow];
+        };
+        const v16i z = {0};
+        rd(0, 0);
+        rd(1, 1);
+        rds(0, 0);
+        v16i Sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[0], B[0], z, 0, 0, 0);
 #pragma unroll
-                for (int d = 0; d < 9; d++) dw[d] = rp[d];
-                sbits = dw[0] & 0xFFFFu;
-#pragma unroll
-                for (int d = 0; d < 8; d++) q[d] = __builtin_amdgcn_alignbit(dw[d + 1], dw[d], 16u);
-            } else {
-                sbits = rp[8] >> 16;
-#pragma unroll
-                for (int d = 0; d < 8; d++) q[d] = rp[9 + d];
-            }
-            u32x4 lo = {q[0], q[1], q[2], q[3]}, hi = {q[4], q[5], q[6], q[7]};
-            *reinterpret_cast<u32x4 *>(sW + row * kMmqKB + 16 * ((2 * b) ^ (row & 7))) = lo;
-            *reinterpret_cast<u32x4 *>(sW + row * kMmqKB + 16 * ((2 * b + 1) ^ (row & 7))) = hi;
-            sDW[b][row] = half_bits_to_float(sbits);
-        }
-        __syncthreads();
-#pragma unroll 2
         for (int b = 0; b < kMmqBlocks; b++) {
-            int c = 2 * b + khalf;
-            v4i a = *reinterpret_cast<const v4i *>(sX + arow * kMmqKB + 16 * (c ^ (arow & 7)));
-            v4i bb = *reinterpret_cast<const v4i *>(sW + brow * kMmqKB + 16 * (c ^ (brow & 7)));
-            v16i z = {0};
-            v16i S = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bb, z, 0, 0, 0);
-            float dw = sDW[b][brow];
-            const float *dxp = &sDX[b][wm * 32 + 4 * khalf];
+            if (b + 2 < kMmqBlocks) rd(b + 2, (b + 2) % 3);
+            const v16i Sc = Sn;
+            if (b + 1 < kMmqBlocks) {
+                Sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[(b + 1) % 3], B[(b + 1) % 3], z, 0, 0, 0);
+                rds(b + 1, (b + 1) & 1);
+            }
+            // Issue that MFMA before the fold below (it then runs under the
+            // fold's VALU work instead of stalling the next block's fold).
+            asm volatile("" : "+v"(Sn));
+            const float dw = DW[b & 1];
 #pragma unroll
             for (int qd = 0; qd < 4; qd++) {
-                float4 dx = *reinterpret_cast<const float4 *>(dxp + 8 * qd);
-                acc[4 * qd + 0] = __builtin_fmaf((float)S[4 * qd + 0], dx.x * dw, acc[4 * qd + 0]);
-                acc[4 * qd + 1] = __builtin_fmaf((float)S[4 * qd + 1], dx.y * dw, acc[4 * qd + 1]);
-                acc[4 * qd + 2] = __builtin_fmaf((float)S[4 * qd + 2], dx.z * dw, acc[4 * qd + 2]);
-                acc[4 * qd + 3] = __builtin_fmaf((float)S[4 * qd + 3], dx.w * dw, acc[4 * qd + 3]);
+                const float4 dx = DX[b & 1][qd];
+                acc[4 * qd + 0] = __builtin_fmaf((float)Sc[4 * qd + 0], dx.x * dw, acc[4 * qd + 0]);
+                acc[4 * qd + 1] = __builtin_fmaf((float)Sc[4 * qd + 1], dx.y * dw, acc[4 * qd + 1]);
+                acc[4 * qd + 2] = __builtin_fmaf((float)Sc[4 * qd + 2], dx.z * dw, acc[4 * qd + 2]);
+                acc[4 * qd + 3] = __builtin_fmaf((float)Sc[4 * qd + 3], dx.w * dw, acc[4 * qd + 3]);
             }
+            // Keep each block's group (reads for b+2, MFMA and scales for b+1,
+            // fold of b) in this order: an empty asm that reads and writes the
+            // accumulators stops the compiler from hoisting every block's loads
+            // and MFMAs to the top (which costs registers and serializes the
+            // fold behind them).  The empty asm emits no instruction.
+            asm volatile("" : "+v"(acc) :: "memory");
         }
+    };
+
+    MmqRegs R0, R1;
+    load_stage(R0, 0);
+    if (nstage > 1) load_stage(R1, 1);
+    store_stage(st[0], R0);
+    __syncthreads();
+    for (int kc = 0; kc < nstage; kc += 2) {
+        // st[0] holds stage kc; R1 holds stage kc+1 (in flight)
+        if (kc + 2 < nstage) load_stage(R0, kc + 2);
+        compute_stage(st[0]);
+        if (kc + 1 < nstage) store_stage(st[1], R1);
         __syncthreads();
+        if (kc + 1 < nstage) {
+            if (kc + 3 < nstage) load_stage(R1, kc + 3);
+            compute_stage(st[1]);
+            if (kc + 2 < nstage) store_stage(st[0], R0);
+            __syncthreads();
+        }
     }
 
     // Output element (row 8*(v/4) + 4*khalf + v%4, column lane%32) of the wave tile.
