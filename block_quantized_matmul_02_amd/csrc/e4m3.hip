@@ -19,7 +19,11 @@
 //
 // The GEMM uses v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales
 // (E8M0 127 = 2^0): 32x32 outputs per 64-deep step, f32 accumulation, the
-// folded scale applied once in the epilogue.
+// folded scale applied once in the epilogue.  Workgroup tile 128 x 128 (4
+// waves of 64 x 64); k staged 128 at a time in double-buffered LDS with padded
+// 144-byte rows (conflict-free reads, immediate offsets), global loads two
+// stages ahead in registers, operand reads for the next 64-deep step issued
+// while the current step's four MFMAs run.
 #include "bqmm_internal.h"
 
 namespace bqm {
@@ -101,20 +105,29 @@ __global__ __launch_bounds__(256) void e4m3_quantize_kernel(const float4 *__rest
 
 constexpr int kF8BM = 128;
 constexpr int kF8BN = 128;
-constexpr int kF8KB = 128;        // k per LDS stage (two 64-deep MFMA steps)
-constexpr int kF8Threads = 256;   // 4 waves, 2 x 2, each 64 x 64
+constexpr int kF8KB = 128;                 // k per LDS stage (two 64-deep MFMA steps)
+constexpr int kF8Threads = 256;            // 4 waves, 2 x 2, each 64 x 64
+constexpr int kF8RowStride = kF8KB + 16;   // 144: padded LDS row (conflict-free, immediate offsets)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t f8_rsrc(const void *base, int64_t bytes) {
     uint32_t b = bytes <= 0 ? 0u : (bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0u : (uint32_t)bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)b, 0x00020000);
 }
 
+struct F8Stage {
+    uint8_t a[kF8BM * kF8RowStride];
+    uint8_t b[kF8BN * kF8RowStride];
+};
+
+struct F8Regs {
+    u32x4 a[4], b[4];
+};
+
 __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__restrict__ w,
                                                              const uint8_t *__restrict__ xq,
                                                              const float *__restrict__ scales, float *__restrict__ y,
                                                              int m, int k, int n) {
-    __shared__ __attribute__((aligned(16))) uint8_t sA[kF8BM * kF8KB];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[kF8BN * kF8KB];
+    __shared__ __attribute__((aligned(16))) F8Stage st[2];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -126,24 +139,30 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
     const __amdgpu_buffer_rsrc_t rA = f8_rsrc(xq + (int64_t)m0 * k, (int64_t)(m - m0) * k);
     const __amdgpu_buffer_rsrc_t rB = f8_rsrc(w + (int64_t)n0 * k, (int64_t)(n - n0) * k);
 
-    u32x4 ra[4], rb[4];
-    auto load_stage = [&](int kc) {
+    // Thread slots: chunk q = tid + 256*s -> row q>>3, 16-byte chunk q&7.  The
+    // stage offset is a uniform scalar added by the buffer load.
+    uint32_t goff[4];
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+        const int q = tid + 256 * s;
+        goff[s] = (uint32_t)((q >> 3) * k + 16 * (q & 7));
+    }
+    const int lrow = tid >> 3, lchunk = tid & 7;   // LDS slot of s = 0; s adds 32 rows
+    auto load_stage = [&](F8Regs &R, int kc) {
+        const int so = kc * kF8KB;
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-            int q = tid + 256 * s;
-            int row = q >> 3, c = q & 7;
-            uint32_t off = (uint32_t)(row * k + kc * kF8KB + 16 * c);
-            ra[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0));
-            rb[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0));
+            R.a[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, goff[s], so, 0));
+            R.b[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, goff[s], so, 0));
         }
     };
-    auto store_stage = [&]() {
+    auto store_stage = [&](F8Stage &S, const F8Regs &R) {
+        uint8_t *pa = S.a + lrow * kF8RowStride + 16 * lchunk;
+        uint8_t *pb = S.b + lrow * kF8RowStride + 16 * lchunk;
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-            int q = tid + 256 * s;
-            int row = q >> 3, c = q & 7;
-            *reinterpret_cast<u32x4 *>(sA + row * kF8KB + 16 * (c ^ (row & 7))) = ra[s];
-            *reinterpret_cast<u32x4 *>(sB + row * kF8KB + 16 * (c ^ (row & 7))) = rb[s];
+            *reinterpret_cast<u32x4 *>(pa + s * 32 * kF8RowStride) = R.a[s];
+            *reinterpret_cast<u32x4 *>(pb + s * 32 * kF8RowStride) = R.b[s];
         }
     };
 
@@ -156,48 +175,65 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
     const int khalf = lane >> 5;
-    load_stage(0);
-    for (int kc = 0; kc < nstage; kc++) {
-        store_stage();
-        __syncthreads();
-        if (kc + 1 < nstage) load_stage(kc + 1);
-#pragma unroll
-        for (int ks = 0; ks < kF8KB / 64; ks++) {
-            const int c0 = ks * 4 + 2 * khalf;   // first 16-byte chunk of this lane's 32 k-values
-            v8i a[2], b[2];
+    // Lane l supplies row l%32 of each 32-row operand tile and k values
+    // 32*(l/32) .. +31 of the 64-deep step (the same k set for A and B).
+    auto compute_stage = [&](const F8Stage &S) {
+        const uint8_t *pa = S.a + (wm * 64 + (lane & 31)) * kF8RowStride + 32 * khalf;
+        const uint8_t *pb = S.b + (wn * 64 + (lane & 31)) * kF8RowStride + 32 * khalf;
+        v8i a[2][2], b[2][2];   // [k-step parity][tile]
+        auto rd = [&](int ks, int slot) {
 #pragma unroll
             for (int i = 0; i < 2; i++) {
-                int row = wm * 64 + i * 32 + (lane & 31);
-                u32x4 lo = *reinterpret_cast<const u32x4 *>(sA + row * kF8KB + 16 * (c0 ^ (row & 7)));
-                u32x4 hi = *reinterpret_cast<const u32x4 *>(sA + row * kF8KB + 16 * ((c0 + 1) ^ (row & 7)));
-                a[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                const u32x4 lo = *reinterpret_cast<const u32x4 *>(pa + i * 32 * kF8RowStride + 64 * ks);
+                const u32x4 hi = *reinterpret_cast<const u32x4 *>(pa + i * 32 * kF8RowStride + 64 * ks + 16);
+                a[slot][i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                const u32x4 lo2 = *reinterpret_cast<const u32x4 *>(pb + i * 32 * kF8RowStride + 64 * ks);
+                const u32x4 hi2 = *reinterpret_cast<const u32x4 *>(pb + i * 32 * kF8RowStride + 64 * ks + 16);
+                b[slot][i] = v8i{(int)lo2[0], (int)lo2[1], (int)lo2[2], (int)lo2[3], (int)hi2[0], (int)hi2[1], (int)hi2[2], (int)hi2[3]};
             }
+        };
+        rd(0, 0);
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                int row = wn * 64 + j * 32 + (lane & 31);
-                u32x4 lo = *reinterpret_cast<const u32x4 *>(sB + row * kF8KB + 16 * (c0 ^ (row & 7)));
-                u32x4 hi = *reinterpret_cast<const u32x4 *>(sB + row * kF8KB + 16 * ((c0 + 1) ^ (row & 7)));
-                b[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            }
+        for (int ks = 0; ks < kF8KB / 64; ks++) {
+            if (ks + 1 < kF8KB / 64) rd(ks + 1, (ks + 1) & 1);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
                 for (int j = 0; j < 2; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks & 1][i], b[ks & 1][j], acc[i][j], 0, 0,
+                                                                              0, 127, 0, 127);
         }
+    };
+
+    F8Regs R0, R1;
+    load_stage(R0, 0);
+    if (nstage > 1) load_stage(R1, 1);
+    store_stage(st[0], R0);
+    __syncthreads();
+    for (int kc = 0; kc < nstage; kc += 2) {
+        // st[0] holds stage kc; R1 holds stage kc+1 (in flight)
+        if (kc + 2 < nstage) load_stage(R0, kc + 2);
+        compute_stage(st[0]);
+        if (kc + 1 < nstage) store_stage(st[1], R1);
         __syncthreads();
+        if (kc + 1 < nstage) {
+            if (kc + 3 < nstage) load_stage(R1, kc + 3);
+            compute_stage(st[1]);
+            if (kc + 2 < nstage) store_stage(st[0], R0);
+            __syncthreads();
+        }
     }
 
     const float sc = scales[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) {
-        int col = n0 + wn * 64 + j * 32 + (lane & 31);
+        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
         if (col >= n) continue;
 #pragma unroll
         for (int i = 0; i < 2; i++) {
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+                const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
                 if (row < m) y[(int64_t)row * n + col] = acc[i][j][v] * sc;
             }
         }

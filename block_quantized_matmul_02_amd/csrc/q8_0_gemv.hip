@@ -12,7 +12,7 @@
 //    Each row is handled by L lanes (L = next power of two >= P, at most
 //    64); lane i of the row owns pairs i, i+L, ...  A wave covers G = 64/L
 //    rows per row-step.
-//  * A wave streams a tile of RT whole rows (<= 16 KiB) with 16-byte buffer
+//  * A wave streams a tile of RT whole rows (<= 12 KiB) with 16-byte buffer
 //    loads: slot s of lane l loads chunk 64*s + l of the tile, so every load
 //    instruction reads 1 KiB of consecutive bytes.  Buffer loads check the
 //    range in hardware: rows past n and unused slots read zeros, never fault.
@@ -36,9 +36,9 @@ namespace bqm {
 
 constexpr int kGemvThreads = 256;      // 4 waves, each streaming its own tiles
 constexpr int kGemvWaves = kGemvThreads / 64;
-constexpr int kSlots = 16;             // 16 x 1 KiB per tile
+constexpr int kSlots = 12;             // 12 x 1 KiB per tile (2 rows of K=4096; 3 workgroups per CU)
 constexpr int kTileBytes = kSlots * 1024;
-constexpr int kMaxPairsPerSeg = 240;   // 240 * 68 = 16320 bytes <= one tile
+constexpr int kMaxPairsPerSeg = 180;   // 180 * 68 = 12240 bytes <= one tile
 constexpr int kActLdsMax = 98304;      // activation bytes staged per workgroup
 // Cache policy of the weight loads: non-temporal.  Every weight byte is read
 // exactly once, so keeping it out of the caches frees them for the activations
