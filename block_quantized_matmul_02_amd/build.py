@@ -5,7 +5,7 @@ shared library next to this file.  Flags:
   -ffp-contract=off   floating-point contraction only where a kernel writes
                       an explicit fma, so results do not depend on inlining;
   -packed-fp32-ops    removed from the target features: no packed f32 VALU;
-  -amdgpu-mfma-vgpr-form=1
+  -amdgpu-mfma-vgpr-form=1 (MMQ only)
                       MFMA sources and results in ordinary VGPRs, so the
                       VALU fold reads the int32 block sums without copies.
 """
@@ -34,15 +34,20 @@ HIPFLAGS = [
     "-fPIC",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE,
     "-I", CSRC,
 ]
+# Per-source extra flags.  The MMQ folds each MFMA result on the VALU, so its
+# MFMAs write ordinary VGPRs; the e4m3 GEMM keeps its large accumulator tiles
+# in AGPRs (the default form).
+EXTRA = {
+    "q8_0_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *HIPFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *HIPFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -19,11 +19,14 @@
 //
 // The GEMM uses v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales
 // (E8M0 127 = 2^0): 32x32 outputs per 64-deep step, f32 accumulation, the
-// folded scale applied once in the epilogue.  Workgroup tile 128 x 128 (4
-// waves of 64 x 64); k staged 128 at a time in double-buffered LDS with padded
-// 144-byte rows (conflict-free reads, immediate offsets), global loads two
-// stages ahead in registers, operand reads for the next 64-deep step issued
-// while the current step's four MFMAs run.
+// folded scale applied once in the epilogue.  Workgroup tile 128 x 64*NT
+// (4 waves of 64 x 32*NT, NT = 2..5 chosen per shape so the tiles spread
+// evenly over the CUs: m=512, N=20480 takes NT=5, 256 tiles of 128 x 320,
+// one per CU); k staged 128 at a time in double-buffered LDS with padded
+// 144-byte rows (conflict-free reads, immediate offsets), global loads one
+// stage ahead in registers, operand reads for the next 64-deep step slotted
+// between the current step's MFMAs.  Accumulators live in AGPRs (up to 160
+// per lane), leaving the VGPRs to the operand and load pipelines.
 #include "bqmm_internal.h"
 
 namespace bqm {
@@ -103,10 +106,9 @@ __global__ __launch_bounds__(256) void e4m3_quantize_kernel(const float4 *__rest
 
 // ------------------------------------------------------------------ GEMM
 
-constexpr int kF8BM = 128;
-constexpr int kF8BN = 128;
+constexpr int kF8BM = 128;                 // workgroup tile rows (tokens)
 constexpr int kF8KB = 128;                 // k per LDS stage (two 64-deep MFMA steps)
-constexpr int kF8Threads = 256;            // 4 waves, 2 x 2, each 64 x 64
+constexpr int kF8Threads = 256;            // 4 waves, 2 x 2
 constexpr int kF8RowStride = kF8KB + 16;   // 144: padded LDS row (conflict-free, immediate offsets)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t f8_rsrc(const void *base, int64_t bytes) {
@@ -114,83 +116,87 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t f8_rsrc(const void *base, int6
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)b, 0x00020000);
 }
 
+// Workgroup tile 128 x 64*NT: 4 waves in 2 x 2, each 64 x 32*NT (2 x NT
+// 32x32 MFMA tiles).  A wave reads 2 + NT operand tiles per 64-deep step
+// for 2*NT MFMAs, so larger NT means less LDS traffic per MFMA.
+template <int NT>
 struct F8Stage {
     uint8_t a[kF8BM * kF8RowStride];
-    uint8_t b[kF8BN * kF8RowStride];
+    uint8_t b[64 * NT * kF8RowStride];
 };
 
+template <int NT>
 struct F8Regs {
-    u32x4 a[4], b[4];
+    u32x4 a[4];        // 128 rows x 128 bytes = 1024 chunks, 4 per thread
+    u32x4 b[2 * NT];   // 64*NT rows x 128 bytes, 2*NT per thread
 };
 
+template <int NT>
 __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__restrict__ w,
                                                              const uint8_t *__restrict__ xq,
                                                              const float *__restrict__ scales, float *__restrict__ y,
                                                              int m, int k, int n) {
-    __shared__ __attribute__((aligned(16))) F8Stage st[2];
+    constexpr int BN = 64 * NT;
+    __shared__ __attribute__((aligned(16))) F8Stage<NT> st[2];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = blockIdx.x * kF8BN;
+    const int n0 = blockIdx.x * BN;
     const int m0 = blockIdx.y * kF8BM;
     const int nstage = k / kF8KB;
 
     const __amdgpu_buffer_rsrc_t rA = f8_rsrc(xq + (int64_t)m0 * k, (int64_t)(m - m0) * k);
     const __amdgpu_buffer_rsrc_t rB = f8_rsrc(w + (int64_t)n0 * k, (int64_t)(n - n0) * k);
 
-    // Thread slots: chunk q = tid + 256*s -> row q>>3, 16-byte chunk q&7.  The
-    // stage offset is a uniform scalar added by the buffer load.
-    uint32_t goff[4];
-#pragma unroll
-    for (int s = 0; s < 4; s++) {
-        const int q = tid + 256 * s;
-        goff[s] = (uint32_t)((q >> 3) * k + 16 * (q & 7));
-    }
-    const int lrow = tid >> 3, lchunk = tid & 7;   // LDS slot of s = 0; s adds 32 rows
-    auto load_stage = [&](F8Regs &R, int kc) {
+    // Thread slots: chunk q = tid + 256*s -> row q>>3 (s adds 32 rows), 16-byte
+    // chunk q&7.  The stage offset is a uniform scalar added by the load.
+    const uint32_t goff = (uint32_t)((tid >> 3) * k + 16 * (tid & 7));
+    const uint32_t grow32 = (uint32_t)(32 * k);
+    auto load_stage = [&](F8Regs<NT> &R, int kc) {
         const int so = kc * kF8KB;
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-            R.a[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, goff[s], so, 0));
-            R.b[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, goff[s], so, 0));
-        }
-    };
-    auto store_stage = [&](F8Stage &S, const F8Regs &R) {
-        uint8_t *pa = S.a + lrow * kF8RowStride + 16 * lchunk;
-        uint8_t *pb = S.b + lrow * kF8RowStride + 16 * lchunk;
+        for (int s = 0; s < 4; s++)
+            R.a[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, goff + s * grow32, so, 0));
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-            *reinterpret_cast<u32x4 *>(pa + s * 32 * kF8RowStride) = R.a[s];
-            *reinterpret_cast<u32x4 *>(pb + s * 32 * kF8RowStride) = R.b[s];
-        }
+        for (int s = 0; s < 2 * NT; s++)
+            R.b[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, goff + s * grow32, so, 0));
+    };
+    const int lds_off = (tid >> 3) * kF8RowStride + 16 * (tid & 7);
+    auto store_stage = [&](F8Stage<NT> &S, const F8Regs<NT> &R) {
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+            *reinterpret_cast<u32x4 *>(S.a + lds_off + s * 32 * kF8RowStride) = R.a[s];
+#pragma unroll
+        for (int s = 0; s < 2 * NT; s++)
+            *reinterpret_cast<u32x4 *>(S.b + lds_off + s * 32 * kF8RowStride) = R.b[s];
     };
 
-    v16f acc[2][2];
+    v16f acc[2][NT];
 #pragma unroll
     for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < NT; j++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
     const int khalf = lane >> 5;
     // Lane l supplies row l%32 of each 32-row operand tile and k values
     // 32*(l/32) .. +31 of the 64-deep step (the same k set for A and B).
-    auto compute_stage = [&](const F8Stage &S) {
+    auto compute_stage = [&](const F8Stage<NT> &S) {
         const uint8_t *pa = S.a + (wm * 64 + (lane & 31)) * kF8RowStride + 32 * khalf;
-        const uint8_t *pb = S.b + (wn * 64 + (lane & 31)) * kF8RowStride + 32 * khalf;
-        v8i a[2][2], b[2][2];   // [k-step parity][tile]
+        const uint8_t *pb = S.b + (wn * 32 * NT + (lane & 31)) * kF8RowStride + 32 * khalf;
+        v8i a[2][2], b[2][NT];   // [k-step parity][tile]
+        auto ld8 = [](const uint8_t *p) {
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(p);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + 16);
+            return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        };
         auto rd = [&](int ks, int slot) {
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const u32x4 lo = *reinterpret_cast<const u32x4 *>(pa + i * 32 * kF8RowStride + 64 * ks);
-                const u32x4 hi = *reinterpret_cast<const u32x4 *>(pa + i * 32 * kF8RowStride + 64 * ks + 16);
-                a[slot][i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                const u32x4 lo2 = *reinterpret_cast<const u32x4 *>(pb + i * 32 * kF8RowStride + 64 * ks);
-                const u32x4 hi2 = *reinterpret_cast<const u32x4 *>(pb + i * 32 * kF8RowStride + 64 * ks + 16);
-                b[slot][i] = v8i{(int)lo2[0], (int)lo2[1], (int)lo2[2], (int)lo2[3], (int)hi2[0], (int)hi2[1], (int)hi2[2], (int)hi2[3]};
-            }
+            for (int i = 0; i < 2; i++) a[slot][i] = ld8(pa + i * 32 * kF8RowStride + 64 * ks);
+#pragma unroll
+            for (int j = 0; j < NT; j++) b[slot][j] = ld8(pb + j * 32 * kF8RowStride + 64 * ks);
         };
         rd(0, 0);
 #pragma unroll
@@ -199,35 +205,50 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
-                for (int j = 0; j < 2; j++)
+                for (int j = 0; j < NT; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks & 1][i], b[ks & 1][j], acc[i][j], 0, 0,
                                                                               0, 127, 0, 127);
         }
     };
 
-    F8Regs R0, R1;
+    // One register copy of the next stage: its global loads are issued at the
+    // top of an iteration and written to the other LDS buffer at the bottom.
+    // The loop body is a single basic block (the last stage is peeled) so
+    // the scheduling groups below can order it: global loads first, then the
+    // operand reads of the first 64-deep step, then the MFMAs one at a time
+    // with the second step's operand reads and then the stage stores slotted
+    // between them, so LDS latency hides behind the matrix pipe (one wave
+    // per SIMD leaves no other wave to hide it).  Masks: 0x020 VMEM read,
+    // 0x100 DS read, 0x200 DS write, 0x008 MFMA.
+    F8Regs<NT> R0;
     load_stage(R0, 0);
-    if (nstage > 1) load_stage(R1, 1);
     store_stage(st[0], R0);
     __syncthreads();
-    for (int kc = 0; kc < nstage; kc += 2) {
-        // st[0] holds stage kc; R1 holds stage kc+1 (in flight)
-        if (kc + 2 < nstage) load_stage(R0, kc + 2);
-        compute_stage(st[0]);
-        if (kc + 1 < nstage) store_stage(st[1], R1);
-        __syncthreads();
-        if (kc + 1 < nstage) {
-            if (kc + 3 < nstage) load_stage(R1, kc + 3);
-            compute_stage(st[1]);
-            if (kc + 2 < nstage) store_stage(st[0], R0);
-            __syncthreads();
+#pragma unroll 1
+    for (int kc = 0; kc + 1 < nstage; kc++) {
+        load_stage(R0, kc + 1);
+        compute_stage(st[kc & 1]);
+        store_stage(st[(kc + 1) & 1], R0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 4 + 2 * NT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * NT, 0);
+#pragma unroll
+        for (int r = 0; r < 2 * NT; r++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
+#pragma unroll
+        for (int r = 0; r < 2 * NT; r++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+        }
+        __syncthreads();
     }
+    compute_stage(st[(nstage - 1) & 1]);
 
     const float sc = scales[2];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < NT; j++) {
+        const int col = n0 + wn * 32 * NT + j * 32 + (lane & 31);
         if (col >= n) continue;
 #pragma unroll
         for (int i = 0; i < 2; i++) {
@@ -238,6 +259,33 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
             }
         }
     }
+}
+
+// Pick the tile width (NT) that needs the fewest rounds of workgroups over
+// the CUs, weighting each round by its tile width; ties go to the wider tile
+// (less LDS traffic per MFMA).
+static int pick_nt(int m, int n, int cus) {
+    int best = 5;
+    int64_t best_cost = -1;
+    for (int nt = 5; nt >= 2; nt--) {
+        const int64_t tiles = (int64_t)((m + kF8BM - 1) / kF8BM) * ((n + 64 * nt - 1) / (64 * nt));
+        const int64_t rounds = (tiles + cus - 1) / cus;
+        const int64_t cost = rounds * nt;
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = nt;
+        }
+    }
+    return best;
+}
+
+template <int NT>
+static int launch_f8(const uint8_t *w, const uint8_t *xq, const float *scales, float *y, int m, int k, int n,
+                     hipStream_t s) {
+    dim3 grid((n + 64 * NT - 1) / (64 * NT), (m + kF8BM - 1) / kF8BM);
+    if (grid.y > 65535) return BQM_EUNSUPPORTED;
+    hipLaunchKernelGGL(e4m3_gemm_kernel<NT>, grid, dim3(kF8Threads), 0, s, w, xq, scales, y, m, k, n);
+    return launch_status();
 }
 
 }  // namespace bqm
@@ -282,9 +330,14 @@ extern "C" int bqm_e4m3_gemm(const uint8_t *w, const uint8_t *xq, const float *s
     if (m < 1 || k < 128 || n < 1) return BQM_EINVAL;
     if (k % 128 != 0) return BQM_EUNSUPPORTED;
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(scales, 4) || !aligned(y, 4)) return BQM_EUNSUPPORTED;
-    if ((int64_t)kF8BM * k > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
-    dim3 grid((n + kF8BN - 1) / kF8BN, (m + kF8BM - 1) / kF8BM);
-    if (grid.y > 65535) return BQM_EUNSUPPORTED;
-    hipLaunchKernelGGL(e4m3_gemm_kernel, grid, dim3(kF8Threads), 0, as_stream(stream), w, xq, scales, y, m, k, n);
-    return launch_status();
+    if ((int64_t)kF8BM * k > 0x7FFFFFF0ll || (int64_t)320 * k > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    hipStream_t s = as_stream(stream);
+    switch (pick_nt(m, n, cus)) {
+        case 2: return launch_f8<2>(w, xq, scales, y, m, k, n, s);
+        case 3: return launch_f8<3>(w, xq, scales, y, m, k, n, s);
+        case 4: return launch_f8<4>(w, xq, scales, y, m, k, n, s);
+        default: return launch_f8<5>(w, xq, scales, y, m, k, n, s);
+    }
 }
