@@ -12,6 +12,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQK = 32;          // values per quantization block

@@ -53,9 +53,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mmq_rsrc(const void *base, int
 struct MmqStage {
     uint8_t x[kMmqBM * kMmqRowStride];   // activation quants, padded rows
     uint8_t w[kMmqBN * kMmqRowStride];   // weight quants, padded rows
-    float dx[kMmqBlocks][kMmqBM];        // d_x per block and token row
-    float dw[kMmqBlocks][kMmqBN];        // d_w per block and weight row
+    // d_x / d_w per block and row; rows padded by 8 floats so that the
+    // stores (8 blocks of a row from neighbouring threads) hit distinct banks
+    float dx[kMmqBlocks][kMmqBM + 8];
+    float dw[kMmqBlocks][kMmqBN + 8];
 };
+static_assert(2 * sizeof(MmqStage) * 2 <= 160 * 1024, "two workgroups per CU");
 
 // Global loads of one stage, held in registers until written to LDS.
 struct MmqRegs {
@@ -166,52 +169,54 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
     const int brow = wn * 32 + (lane & 31);   // B operand row (weight row) of this lane
     const int khalf = lane >> 5;
 
-    // One stage: 8 blocks.  Quant operands are read two blocks ahead, the MFMA
-    // and the fold's scales one block ahead, so no LDS or MFMA latency sits in
-    // front of a fold.
+    // One stage: 8 blocks.  Quant operands are read two blocks ahead and the
+    // int8 MFMA runs one block ahead of the fold.  The scale products
+    // d_x[t][b] * d_w[r][b] come from the matrix core as well: one
+    // v_mfma_f32_32x32x1_2b_f32 forms the 32x32 outer products of two blocks
+    // (lanes 0-31 carry block b, lanes 32-63 block b+1; each result element
+    // is one correctly rounded f32 product, as a VALU multiply would give),
+    // in the same register layout as the int32 block sums.  That leaves two
+    // VALU ops per output and block: convert S, then fma into the
+    // accumulator.  The outer products of a pair are issued one pair ahead.
     auto compute_stage = [&](const MmqStage &S) {
         v4i A[3], B[3];
-        float4 DX[2][4];
-        float DW[2];
         const uint8_t *xa = S.x + arow * kMmqRowStride + 16 * khalf;
         const uint8_t *wb = S.w + brow * kMmqRowStride + 16 * khalf;
         auto rd = [&](int b, int slot) {
             A[slot] = *reinterpret_cast<const v4i *>(xa + 32 * b);
             B[slot] = *reinterpret_cast<const v4i *>(wb + 32 * b);
         };
-        auto rds = [&](int b, int slot) {
-            const float *dxp = &S.dx[b][wm * 32 + 4 * khalf];
+        // scale operands of the 4 block pairs: d_x[b + khalf][token], d_w[b + khalf][weight row]
+        float SA[kMmqBlocks / 2], SB[kMmqBlocks / 2];
 #pragma unroll
-            for (int qd = 0; qd < 4; qd++) DX[slot][qd] = *reinterpret_cast<const float4 *>(dxp + 8 * qd);
-            DW[slot] = S.dw[b][brow];
-        };
+        for (int p = 0; p < kMmqBlocks / 2; p++) {
+            SA[p] = S.dx[2 * p + khalf][arow];
+            SB[p] = S.dw[2 * p + khalf][brow];
+        }
         const v16i z = {0};
+        const v32f z32 = {0};
+        v32f P[2];
         rd(0, 0);
         rd(1, 1);
-        rds(0, 0);
+        P[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(SA[0], SB[0], z32, 0, 0, 0);
         v16i Sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[0], B[0], z, 0, 0, 0);
 #pragma unroll
         for (int b = 0; b < kMmqBlocks; b++) {
             if (b + 2 < kMmqBlocks) rd(b + 2, (b + 2) % 3);
             const v16i Sc = Sn;
-            if (b + 1 < kMmqBlocks) {
-                Sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[(b + 1) % 3], B[(b + 1) % 3], z, 0, 0, 0);
-                rds(b + 1, (b + 1) & 1);
-            }
-            // Issue that MFMA before the fold below (it then runs under the
+            if (b + 1 < kMmqBlocks) Sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[(b + 1) % 3], B[(b + 1) % 3], z, 0, 0, 0);
+            if ((b & 1) == 0 && b + 2 < kMmqBlocks)
+                P[((b + 2) >> 1) & 1] =
+                    __builtin_amdgcn_mfma_f32_32x32x1f32(SA[(b + 2) >> 1], SB[(b + 2) >> 1], z32, 0, 0, 0);
+            // Issue those MFMAs before the fold below (they then run under the
             // fold's VALU work instead of stalling the next block's fold).
             asm volatile("" : "+v"(Sn));
-            const float dw = DW[b & 1];
+            const v32f &Pc = P[(b >> 1) & 1];
+            const int h = 16 * (b & 1);
 #pragma unroll
-            for (int qd = 0; qd < 4; qd++) {
-                const float4 dx = DX[b & 1][qd];
-                acc[4 * qd + 0] = __builtin_fmaf((float)Sc[4 * qd + 0], dx.x * dw, acc[4 * qd + 0]);
-                acc[4 * qd + 1] = __builtin_fmaf((float)Sc[4 * qd + 1], dx.y * dw, acc[4 * qd + 1]);
-                acc[4 * qd + 2] = __builtin_fmaf((float)Sc[4 * qd + 2], dx.z * dw, acc[4 * qd + 2]);
-                acc[4 * qd + 3] = __builtin_fmaf((float)Sc[4 * qd + 3], dx.w * dw, acc[4 * qd + 3]);
-            }
-            // Keep each block's group (reads for b+2, MFMA and scales for b+1,
-            // fold of b) in this order: an empty asm that reads and writes the
+            for (int v = 0; v < 16; v++) acc[v] = __builtin_fmaf((float)Sc[v], Pc[h + v], acc[v]);
+            // Keep each block's group (reads for b+2, MFMAs for b+1, fold of
+            // b) in this order: an empty asm that reads and writes the
             // accumulators stops the compiler from hoisting every block's loads
             // and MFMAs to the top (which costs registers and serializes the
             // fold behind them).  The empty asm emits no instruction.
@@ -219,19 +224,24 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
         }
     };
 
+    // The loads are unconditional (past the last stage they re-read it, an L2
+    // hit): with a branch around them the compiler cannot count the loads in
+    // flight, and its wait before writing the older register buffer to LDS
+    // would then also wait for the loads just issued.
     MmqRegs R0, R1;
+    const int last = nstage - 1;
     load_stage(R0, 0);
-    if (nstage > 1) load_stage(R1, 1);
+    load_stage(R1, min(1, last));
     store_stage(st[0], R0);
     __syncthreads();
     for (int kc = 0; kc < nstage; kc += 2) {
         // st[0] holds stage kc; R1 holds stage kc+1 (in flight)
-        if (kc + 2 < nstage) load_stage(R0, kc + 2);
+        load_stage(R0, min(kc + 2, last));
         compute_stage(st[0]);
         if (kc + 1 < nstage) store_stage(st[1], R1);
         __syncthreads();
         if (kc + 1 < nstage) {
-            if (kc + 3 < nstage) load_stage(R1, kc + 3);
+            load_stage(R1, min(kc + 3, last));
             compute_stage(st[1]);
             if (kc + 2 < nstage) store_stage(st[0], R0);
             __syncthreads();

@@ -36,7 +36,7 @@ namespace bqm {
 
 constexpr int kGemvThreads = 256;      // 4 waves, each streaming its own tiles
 constexpr int kGemvWaves = kGemvThreads / 64;
-constexpr int kSlots = 12;             // 12 x 1 KiB per tile (2 rows of K=4096; 3 workgroups per CU)
+constexpr int kSlots = 9;              // 9 x 1 KiB per tile (2 rows of K=4096, 8.5 KiB)
 constexpr int kTileBytes = kSlots * 1024;
 constexpr int kMaxPairsPerSeg = 180;   // 180 * 68 = 12240 bytes <= one tile
 constexpr int kActLdsMax = 98304;      // activation bytes staged per workgroup
@@ -79,7 +79,9 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     uint8_t *act_q = lds;                                  // [M][k] swizzled per pair
     float *act_d = reinterpret_cast<float *>(lds + M * k);  // [M][nb]
     const int act_bytes = (M * k + M * nb * 4 + 15) & ~15;
-    const int wave = threadIdx.x >> 6;
+    // wave index as a scalar: everything derived from it (tile, segment, buffer
+    // resource) is then wave-uniform and lives in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     uint8_t *tile = lds + act_bytes + wave * kTileBytes;
 
@@ -119,13 +121,16 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         }
     }
 
+    // Issue the loads of work item q.  Items past the wave's last one get an
+    // empty resource: the loads return zeros without touching memory.
     auto issue = [&](u32x4 (&buf)[kSlots], int q) {
         int rt = wid + nwaves * (q / g.nseg);
         int sg = q - (q / g.nseg) * g.nseg;
         int64_t row0 = (int64_t)rt * g.RT;
         const uint8_t *base = w + row0 * w_row_bytes + (int64_t)sg * g.PS * 68;
         int64_t rem = (int64_t)(n - row0) * w_row_bytes - (int64_t)sg * g.PS * 68;
-        uint32_t bytes = rem > 0x7FFFFFF0ll ? 0x7FFFFFF0u : (uint32_t)rem;
+        uint32_t bytes = q >= Q ? 0u : (rem > 0x7FFFFFF0ll ? 0x7FFFFFF0u : (uint32_t)rem);
+        if (q >= Q) base = w;
         __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
 #pragma unroll
         for (int s = 0; s < kSlots; s++) buf[s] = buf_load16(rs, voff[s]);
@@ -145,93 +150,145 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
 #pragma unroll
     for (int t = 0; t < M; t++) acc[t] = 0.0f;
 
+    // One pair (two blocks) of tile row rl, pair pl of the segment, for every
+    // token: a[t] += d_w*d_x*S for both blocks.
+    auto pair_dot = [&](int rl, int pl, int sg, float (&a)[M]) {
+        const uint32_t *pw = reinterpret_cast<const uint32_t *>(tile + rl * (68 * g.PS) + 68 * pl);
+        uint32_t dw[17];
+#pragma unroll
+        for (int d = 0; d < 17; d++) dw[d] = pw[d];
+        int qa[8], qb[8];
+#pragma unroll
+        for (int d = 0; d < 8; d++) {
+            qa[d] = (int)__builtin_amdgcn_alignbit(dw[d + 1], dw[d], 16u);
+            qb[d] = (int)dw[9 + d];
+        }
+        const float da = half_bits_to_float(dw[0]);
+        const float db = half_bits_to_float(dw[8] >> 16);
+        const int p = sg * g.PS + pl;   // pair index in the row
+        const int rot = (p >> 1) & 3;
+#pragma unroll
+        for (int t = 0; t < M; t++) {
+            const uint8_t *ap = act_q + t * k + 64 * p;
+            v4i x0 = *reinterpret_cast<const v4i *>(ap + 16 * ((0 + rot) & 3));
+            v4i x1 = *reinterpret_cast<const v4i *>(ap + 16 * ((1 + rot) & 3));
+            v4i x2 = *reinterpret_cast<const v4i *>(ap + 16 * ((2 + rot) & 3));
+            v4i x3 = *reinterpret_cast<const v4i *>(ap + 16 * ((3 + rot) & 3));
+            float2 dx = *reinterpret_cast<const float2 *>(act_d + t * nb + 2 * p);
+            int sa = 0, sb = 0;
+            sa = __builtin_amdgcn_sdot4(qa[0], x0[0], sa, false);
+            sa = __builtin_amdgcn_sdot4(qa[1], x0[1], sa, false);
+            sa = __builtin_amdgcn_sdot4(qa[2], x0[2], sa, false);
+            sa = __builtin_amdgcn_sdot4(qa[3], x0[3], sa, false);
+            sa = __builtin_amdgcn_sdot4(qa[4], x1[0], sa, false);
+            sa = __builtin_amdgcn_sdot4(qa[5], x1[1], sa, false);
+            sa = __builtin_amdgcn_sdot4(qa[6], x1[2], sa, false);
+            sa = __builtin_amdgcn_sdot4(qa[7], x1[3], sa, false);
+            sb = __builtin_amdgcn_sdot4(qb[0], x2[0], sb, false);
+            sb = __builtin_amdgcn_sdot4(qb[1], x2[1], sb, false);
+            sb = __builtin_amdgcn_sdot4(qb[2], x2[2], sb, false);
+            sb = __builtin_amdgcn_sdot4(qb[3], x2[3], sb, false);
+            sb = __builtin_amdgcn_sdot4(qb[4], x3[0], sb, false);
+            sb = __builtin_amdgcn_sdot4(qb[5], x3[1], sb, false);
+            sb = __builtin_amdgcn_sdot4(qb[6], x3[2], sb, false);
+            sb = __builtin_amdgcn_sdot4(qb[7], x3[3], sb, false);
+            const float sca = da * dx.x;
+            const float scb = db * dx.y;
+            a[t] = __builtin_fmaf((float)sa, sca, a[t]);
+            a[t] = __builtin_fmaf((float)sb, scb, a[t]);
+        }
+    };
+
+    // Sum the L per-lane partials of a row and store y (lane 0 of the row).
+    auto reduce_store = [&](float (&a)[M], int row) {
+#pragma unroll
+        for (int t = 0; t < M; t++) {
+            float v = a[t];
+            v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+            v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+            if (g.L >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+            if (g.L >= 16) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+            if (g.L >= 32) v = swap16_sum(v);
+            if (g.L >= 64) v = swap32_sum(v);
+            if (li == 0 && row < n) y[(int64_t)t * n + row] = v;
+        }
+    };
+
     auto compute = [&](int q) {
-        int rt = wid + nwaves * (q / g.nseg);
-        int sg = q - (q / g.nseg) * g.nseg;
-        int row0 = rt * g.RT;
-        for (int rs = 0; rs < g.RS; rs++) {
-            int rl = rs * g.G + gr;
+        const int rt = wid + nwaves * (q / g.nseg);
+        const int sg = q - (q / g.nseg) * g.nseg;
+        const int row0 = rt * g.RT;
+        if (g.nseg == 1) {
+            // Whole rows.  For one or two tokens, two row-steps at a time as
+            // two independent chains, so the LDS and dot-product latencies of
+            // one overlap the other's (more tokens give enough work per chain
+            // and would double the registers).
+            int rs = 0;
+            for (; M <= 2 && rs + 1 < g.RS; rs += 2) {
+                const int rl0 = rs * g.G + gr, rl1 = rl0 + g.G;
+                float a0[M], a1[M];
+#pragma unroll
+                for (int t = 0; t < M; t++) a0[t] = a1[t] = 0.0f;
+                for (int j = 0; j < g.J; j++) {
+                    const int pl = li + g.L * j;
+                    if (pl < g.PS) {
+                        pair_dot(rl0, pl, 0, a0);
+                        pair_dot(rl1, pl, 0, a1);
+                    }
+                }
+                reduce_store(a0, row0 + rl0);
+                reduce_store(a1, row0 + rl1);
+            }
+            for (; rs < g.RS; rs++) {
+                const int rl = rs * g.G + gr;
+                float a0[M];
+#pragma unroll
+                for (int t = 0; t < M; t++) a0[t] = 0.0f;
+                for (int j = 0; j < g.J; j++) {
+                    const int pl = li + g.L * j;
+                    if (pl < g.PS) pair_dot(rl, pl, 0, a0);
+                }
+                reduce_store(a0, row0 + rl);
+            }
+        } else {
+            // One segment of one row (one row per tile); the accumulators carry
+            // over the row's segments, which this wave takes in order.
             if (sg == 0) {
 #pragma unroll
                 for (int t = 0; t < M; t++) acc[t] = 0.0f;
             }
             for (int j = 0; j < g.J; j++) {
-                int pl = li + g.L * j;
-                if (pl < g.PS) {
-                    const uint32_t *pw = reinterpret_cast<const uint32_t *>(tile + rl * (68 * g.PS) + 68 * pl);
-                    uint32_t dw[17];
-#pragma unroll
-                    for (int d = 0; d < 17; d++) dw[d] = pw[d];
-                    int qa[8], qb[8];
-#pragma unroll
-                    for (int d = 0; d < 8; d++) {
-                        qa[d] = (int)__builtin_amdgcn_alignbit(dw[d + 1], dw[d], 16u);
-                        qb[d] = (int)dw[9 + d];
-                    }
-                    float da = half_bits_to_float(dw[0]);
-                    float db = half_bits_to_float(dw[8] >> 16);
-                    int p = sg * g.PS + pl;   // pair index in the row
-                    int rot = (p >> 1) & 3;
-#pragma unroll
-                    for (int t = 0; t < M; t++) {
-                        const uint8_t *ap = act_q + t * k + 64 * p;
-                        v4i x0 = *reinterpret_cast<const v4i *>(ap + 16 * ((0 + rot) & 3));
-                        v4i x1 = *reinterpret_cast<const v4i *>(ap + 16 * ((1 + rot) & 3));
-                        v4i x2 = *reinterpret_cast<const v4i *>(ap + 16 * ((2 + rot) & 3));
-                        v4i x3 = *reinterpret_cast<const v4i *>(ap + 16 * ((3 + rot) & 3));
-                        float2 dx = *reinterpret_cast<const float2 *>(act_d + t * nb + 2 * p);
-                        int sa = 0, sb = 0;
-                        sa = __builtin_amdgcn_sdot4(qa[0], x0[0], sa, false);
-                        sa = __builtin_amdgcn_sdot4(qa[1], x0[1], sa, false);
-                        sa = __builtin_amdgcn_sdot4(qa[2], x0[2], sa, false);
-                        sa = __builtin_amdgcn_sdot4(qa[3], x0[3], sa, false);
-                        sa = __builtin_amdgcn_sdot4(qa[4], x1[0], sa, false);
-                        sa = __builtin_amdgcn_sdot4(qa[5], x1[1], sa, false);
-                        sa = __builtin_amdgcn_sdot4(qa[6], x1[2], sa, false);
-                        sa = __builtin_amdgcn_sdot4(qa[7], x1[3], sa, false);
-                        sb = __builtin_amdgcn_sdot4(qb[0], x2[0], sb, false);
-                        sb = __builtin_amdgcn_sdot4(qb[1], x2[1], sb, false);
-                        sb = __builtin_amdgcn_sdot4(qb[2], x2[2], sb, false);
-                        sb = __builtin_amdgcn_sdot4(qb[3], x2[3], sb, false);
-                        sb = __builtin_amdgcn_sdot4(qb[4], x3[0], sb, false);
-                        sb = __builtin_amdgcn_sdot4(qb[5], x3[1], sb, false);
-                        sb = __builtin_amdgcn_sdot4(qb[6], x3[2], sb, false);
-                        sb = __builtin_amdgcn_sdot4(qb[7], x3[3], sb, false);
-                        float sca = da * dx.x;
-                        float scb = db * dx.y;
-                        acc[t] = __builtin_fmaf((float)sa, sca, acc[t]);
-                        acc[t] = __builtin_fmaf((float)sb, scb, acc[t]);
-                    }
-                }
+                const int pl = li + g.L * j;
+                if (pl < g.PS) pair_dot(gr, pl, sg, acc);
             }
-            if (sg == g.nseg - 1) {
-                int row = row0 + rl;
-#pragma unroll
-                for (int t = 0; t < M; t++) {
-                    float v = acc[t];
-                    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-                    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-                    if (g.L >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-                    if (g.L >= 16) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
-                    if (g.L >= 32) v = swap16_sum(v);
-                    if (g.L >= 64) v = swap32_sum(v);
-                    if (li == 0 && row < n) y[(int64_t)t * n + row] = v;
-                }
-            }
+            if (sg == g.nseg - 1) reduce_store(acc, row0 + gr);
         }
     };
 
+    // Two items in flight.  Inside the loop both buffers are refilled
+    // unconditionally (the second refill may be the empty item Q), so the
+    // compiler knows that the other buffer's loads are still in flight when a
+    // buffer is staged and waits only for the older loads; a refill behind a
+    // branch would make it wait for all of them.  The last one or two items
+    // are drained after the loop.
     u32x4 bufA[kSlots], bufB[kSlots];
     if (Q > 0) issue(bufA, 0);
     if (Q > 1) issue(bufB, 1);
     stage_activations();
-    for (int q = 0; q < Q; q += 2) {
+    int q = 0;
+    for (; q + 2 < Q; q += 2) {
         stage(bufA);
-        if (q + 2 < Q) issue(bufA, q + 2);
+        issue(bufA, q + 2);
+        compute(q);
+        stage(bufB);
+        issue(bufB, q + 3);
+        compute(q + 1);
+    }
+    if (q < Q) {
+        stage(bufA);
         compute(q);
         if (q + 1 < Q) {
             stage(bufB);
-            if (q + 3 < Q) issue(bufB, q + 3);
             compute(q + 1);
         }
     }
