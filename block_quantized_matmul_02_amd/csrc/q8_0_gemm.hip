@@ -78,8 +78,17 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = blockIdx.x * kMmqBN;
-    const int m0 = blockIdx.y * kMmqBM;
+    // XCD-aware tile order.  Workgroups are handed to the 8 XCDs round-robin
+    // (id % 8), and each XCD has its own L2.  Renumber so that XCD x runs a
+    // contiguous range of tiles, m-tile fastest: the token tiles that share a
+    // weight tile then run together on one XCD and read it once into its L2.
+    const int nm = (m + kMmqBM - 1) / kMmqBM;
+    const int ntiles = gridDim.x;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = ntiles >> 3, extra = ntiles & 7;
+    const int tile = xcd * per + min(xcd, extra) + slot;
+    const int n0 = (tile / nm) * kMmqBN;
+    const int m0 = (tile - (tile / nm) * nm) * kMmqBM;
     const int nb = k / kQK;
     const int nstage = k / kMmqKB;
 
@@ -209,8 +218,11 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
                 P[((b + 2) >> 1) & 1] =
                     __builtin_amdgcn_mfma_f32_32x32x1f32(SA[(b + 2) >> 1], SB[(b + 2) >> 1], z32, 0, 0, 0);
             // Issue those MFMAs before the fold below (they then run under the
-            // fold's VALU work instead of stalling the next block's fold).
-            asm volatile("" : "+v"(Sn));
+            // fold's VALU work instead of stalling the next block's fold): the
+            // empty asm claims to modify the accumulators, so no fold
+            // instruction can move above it, and it reads Sn, so the int8
+            // MFMA cannot move below it.
+            asm volatile("" : "+v"(Sn), "+v"(acc));
             const v32f &Pc = P[(b >> 1) & 1];
             const int h = 16 * (b & 1);
 #pragma unroll
@@ -271,8 +283,9 @@ extern "C" int bqm_q8_0_gemm(const uint8_t *w, int64_t w_row_bytes, const int8_t
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xds, 8) || !aligned(y, 4)) return BQM_EUNSUPPORTED;
     // per-workgroup offsets are 32-bit: 64 rows of activations / weights
     if ((int64_t)kMmqBM * k > 0x7FFFFFF0ll || (int64_t)kMmqBN * w_row_bytes > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
-    dim3 grid((n + kMmqBN - 1) / kMmqBN, (m + kMmqBM - 1) / kMmqBM);
-    if (grid.y > 65535) return BQM_EUNSUPPORTED;
+    const int64_t tiles = (int64_t)((n + kMmqBN - 1) / kMmqBN) * ((m + kMmqBM - 1) / kMmqBM);
+    if (tiles > 0x7FFFFFFF) return BQM_EUNSUPPORTED;
+    dim3 grid((unsigned)tiles);
     hipLaunchKernelGGL(q8_0_gemm_kernel, grid, dim3(kMmqThreads), 0, as_stream(stream), w, w_row_bytes, xq, xds, y, m,
                        k, n);
     return launch_status();

@@ -70,7 +70,7 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kWeightLoadPolicy));
 }
 
-template <int M>
+template <int M, bool SINGLE>
 __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     const uint8_t *__restrict__ w, int64_t w_row_bytes, const int8_t *__restrict__ xq,
     const float *__restrict__ xds, float *__restrict__ y, int k, int n, GemvGeom g) {
@@ -150,9 +150,32 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
 #pragma unroll
     for (int t = 0; t < M; t++) acc[t] = 0.0f;
 
+    // Activation operands of one pair and token: the pair's four 16-byte
+    // chunks of int8 quants (undoing the rotation of the staged copy) and the
+    // two block scales d_x.
+    struct ActPair {
+        v4i x[4];
+        float2 dx;
+    };
+    auto load_act = [&](int t, int p) {
+        ActPair r;
+        const uint8_t *ap = act_q + t * k + 64 * p;
+        const int rot = (p >> 1) & 3;
+#pragma unroll
+        for (int c = 0; c < 4; c++) r.x[c] = *reinterpret_cast<const v4i *>(ap + 16 * ((c + rot) & 3));
+        r.dx = *reinterpret_cast<const float2 *>(act_d + t * nb + 2 * p);
+        return r;
+    };
+
+    // Register copy of this lane's activation pair, filled once the
+    // activations are staged (used when every row gives the lane the same
+    // pair; see compute).
+    ActPair xreg[M <= 2 ? M : 1];
+
     // One pair (two blocks) of tile row rl, pair pl of the segment, for every
-    // token: a[t] += d_w*d_x*S for both blocks.
-    auto pair_dot = [&](int rl, int pl, int sg, float (&a)[M]) {
+    // token: a[t] += d_w*d_x*S for both blocks.  The activation operands come
+    // from LDS, or from xr when the lane's pair is the same for every row.
+    auto pair_dot = [&](int rl, int pl, int sg, float (&a)[M], const ActPair *xr) {
         const uint32_t *pw = reinterpret_cast<const uint32_t *>(tile + rl * (68 * g.PS) + 68 * pl);
         uint32_t dw[17];
 #pragma unroll
@@ -166,34 +189,20 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         const float da = half_bits_to_float(dw[0]);
         const float db = half_bits_to_float(dw[8] >> 16);
         const int p = sg * g.PS + pl;   // pair index in the row
-        const int rot = (p >> 1) & 3;
 #pragma unroll
         for (int t = 0; t < M; t++) {
-            const uint8_t *ap = act_q + t * k + 64 * p;
-            v4i x0 = *reinterpret_cast<const v4i *>(ap + 16 * ((0 + rot) & 3));
-            v4i x1 = *reinterpret_cast<const v4i *>(ap + 16 * ((1 + rot) & 3));
-            v4i x2 = *reinterpret_cast<const v4i *>(ap + 16 * ((2 + rot) & 3));
-            v4i x3 = *reinterpret_cast<const v4i *>(ap + 16 * ((3 + rot) & 3));
-            float2 dx = *reinterpret_cast<const float2 *>(act_d + t * nb + 2 * p);
+            const ActPair x = xr ? xr[t] : load_act(t, p);
             int sa = 0, sb = 0;
-            sa = __builtin_amdgcn_sdot4(qa[0], x0[0], sa, false);
-            sa = __builtin_amdgcn_sdot4(qa[1], x0[1], sa, false);
-            sa = __builtin_amdgcn_sdot4(qa[2], x0[2], sa, false);
-            sa = __builtin_amdgcn_sdot4(qa[3], x0[3], sa, false);
-            sa = __builtin_amdgcn_sdot4(qa[4], x1[0], sa, false);
-            sa = __builtin_amdgcn_sdot4(qa[5], x1[1], sa, false);
-            sa = __builtin_amdgcn_sdot4(qa[6], x1[2], sa, false);
-            sa = __builtin_amdgcn_sdot4(qa[7], x1[3], sa, false);
-            sb = __builtin_amdgcn_sdot4(qb[0], x2[0], sb, false);
-            sb = __builtin_amdgcn_sdot4(qb[1], x2[1], sb, false);
-            sb = __builtin_amdgcn_sdot4(qb[2], x2[2], sb, false);
-            sb = __builtin_amdgcn_sdot4(qb[3], x2[3], sb, false);
-            sb = __builtin_amdgcn_sdot4(qb[4], x3[0], sb, false);
-            sb = __builtin_amdgcn_sdot4(qb[5], x3[1], sb, false);
-            sb = __builtin_amdgcn_sdot4(qb[6], x3[2], sb, false);
-            sb = __builtin_amdgcn_sdot4(qb[7], x3[3], sb, false);
-            const float sca = da * dx.x;
-            const float scb = db * dx.y;
+#pragma unroll
+            for (int d = 0; d < 4; d++) sa = __builtin_amdgcn_sdot4(qa[d], x.x[0][d], sa, false);
+#pragma unroll
+            for (int d = 0; d < 4; d++) sa = __builtin_amdgcn_sdot4(qa[4 + d], x.x[1][d], sa, false);
+#pragma unroll
+            for (int d = 0; d < 4; d++) sb = __builtin_amdgcn_sdot4(qb[d], x.x[2][d], sb, false);
+#pragma unroll
+            for (int d = 0; d < 4; d++) sb = __builtin_amdgcn_sdot4(qb[4 + d], x.x[3][d], sb, false);
+            const float sca = da * x.dx.x;
+            const float scb = db * x.dx.y;
             a[t] = __builtin_fmaf((float)sa, sca, a[t]);
             a[t] = __builtin_fmaf((float)sb, scb, a[t]);
         }
@@ -218,27 +227,36 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         const int rt = wid + nwaves * (q / g.nseg);
         const int sg = q - (q / g.nseg) * g.nseg;
         const int row0 = rt * g.RT;
-        if (g.nseg == 1) {
-            // Whole rows.  For one or two tokens, two row-steps at a time as
-            // two independent chains, so the LDS and dot-product latencies of
-            // one overlap the other's (more tokens give enough work per chain
-            // and would double the registers).
+        if (M <= 2 && g.nseg == 1 && g.J == 1) {
+            // Whole rows with one pair per lane (K <= 4096): the lane's pair,
+            // and so its activation operands, are the same for every row; they
+            // sit in registers.  Two row-steps at a time as two independent
+            // chains, so the LDS and dot-product latencies of one overlap the
+            // other's.
             int rs = 0;
-            for (; M <= 2 && rs + 1 < g.RS; rs += 2) {
+            for (; rs + 1 < g.RS; rs += 2) {
                 const int rl0 = rs * g.G + gr, rl1 = rl0 + g.G;
                 float a0[M], a1[M];
 #pragma unroll
                 for (int t = 0; t < M; t++) a0[t] = a1[t] = 0.0f;
-                for (int j = 0; j < g.J; j++) {
-                    const int pl = li + g.L * j;
-                    if (pl < g.PS) {
-                        pair_dot(rl0, pl, 0, a0);
-                        pair_dot(rl1, pl, 0, a1);
-                    }
+                if (li < g.PS) {
+                    pair_dot(rl0, li, 0, a0, xreg);
+                    pair_dot(rl1, li, 0, a1, xreg);
                 }
                 reduce_store(a0, row0 + rl0);
                 reduce_store(a1, row0 + rl1);
             }
+            if (rs < g.RS) {
+                const int rl = rs * g.G + gr;
+                float a0[M];
+#pragma unroll
+                for (int t = 0; t < M; t++) a0[t] = 0.0f;
+                if (li < g.PS) pair_dot(rl, li, 0, a0, xreg);
+                reduce_store(a0, row0 + rl);
+            }
+        } else if (g.nseg == 1) {
+            // Whole rows, activation operands read from LDS.
+            int rs = 0;
             for (; rs < g.RS; rs++) {
                 const int rl = rs * g.G + gr;
                 float a0[M];
@@ -246,7 +264,7 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
                 for (int t = 0; t < M; t++) a0[t] = 0.0f;
                 for (int j = 0; j < g.J; j++) {
                     const int pl = li + g.L * j;
-                    if (pl < g.PS) pair_dot(rl, pl, 0, a0);
+                    if (pl < g.PS) pair_dot(rl, pl, 0, a0, nullptr);
                 }
                 reduce_store(a0, row0 + rl);
             }
@@ -259,22 +277,41 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
             }
             for (int j = 0; j < g.J; j++) {
                 const int pl = li + g.L * j;
-                if (pl < g.PS) pair_dot(gr, pl, sg, acc);
+                if (pl < g.PS) pair_dot(gr, pl, sg, acc, nullptr);
             }
             if (sg == g.nseg - 1) reduce_store(acc, row0 + gr);
         }
     };
 
-    // Two items in flight.  Inside the loop both buffers are refilled
-    // unconditionally (the second refill may be the empty item Q), so the
-    // compiler knows that the other buffer's loads are still in flight when a
-    // buffer is staged and waits only for the older loads; a refill behind a
-    // branch would make it wait for all of them.  The last one or two items
-    // are drained after the loop.
+    auto load_xreg = [&]() {
+        if (M <= 2 && g.nseg == 1 && g.J == 1 && li < g.PS) {
+#pragma unroll
+            for (int t = 0; t < (M <= 2 ? M : 1); t++) xreg[t] = load_act(t, li);
+        }
+    };
+
     u32x4 bufA[kSlots], bufB[kSlots];
-    if (Q > 0) issue(bufA, 0);
-    if (Q > 1) issue(bufB, 1);
+    if (SINGLE) {
+        // Launched with at most one item per wave: no pipeline (every wave
+        // still stages the activations, which ends in a workgroup barrier).
+        if (Q == 1) issue(bufA, 0);
+        stage_activations();
+        load_xreg();
+        if (Q == 1) {
+            stage(bufA);
+            compute(0);
+        }
+        return;
+    }
+    // Two items in flight.  Every fill is issued unconditionally (a refill
+    // past the last item is empty), so the compiler knows that the other
+    // buffer's loads are still in flight when a buffer is staged and waits
+    // only for the older loads; a fill behind a branch would make it wait for
+    // all of them.  The last one or two items are drained after the loop.
+    issue(bufA, 0);
+    issue(bufB, 1);
     stage_activations();
+    load_xreg();
     int q = 0;
     for (; q + 2 < Q; q += 2) {
         stage(bufA);
@@ -284,13 +321,11 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         issue(bufB, q + 3);
         compute(q + 1);
     }
-    if (q < Q) {
-        stage(bufA);
-        compute(q);
-        if (q + 1 < Q) {
-            stage(bufB);
-            compute(q + 1);
-        }
+    stage(bufA);
+    compute(q);
+    if (q + 1 < Q) {
+        stage(bufB);
+        compute(q + 1);
     }
 }
 
@@ -335,8 +370,11 @@ static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, 
     const int lds_bytes = act_bytes + kGemvWaves * kTileBytes;
     static int attr_done = 0;
     if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, true>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
         attr_done = 1;
     }
@@ -348,8 +386,14 @@ static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, 
     int want = (g.n_row_tiles + kGemvWaves - 1) / kGemvWaves;
     int grid = cus * per_cu;
     if (want < grid) grid = want;
-    hipLaunchKernelGGL(q8_0_gemv_kernel<M>, dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w, w_row_bytes, xq,
-                       xds, y, k, n, g);
+    // every wave holds at most one item: the variant without the pipeline
+    const bool single = (int64_t)g.n_row_tiles * g.nseg <= (int64_t)grid * kGemvWaves;
+    if (single)
+        hipLaunchKernelGGL((q8_0_gemv_kernel<M, true>), dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w,
+                           w_row_bytes, xq, xds, y, k, n, g);
+    else
+        hipLaunchKernelGGL((q8_0_gemv_kernel<M, false>), dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w,
+                           w_row_bytes, xq, xds, y, k, n, g);
     return launch_status();
 }
 
