@@ -43,6 +43,22 @@ def q8_0_bytes(m, k, n):
     return n * (k // 32) * 34 + m * k + m * (k // 32) * 8 + m * n * 4
 
 
+def recorded_traffic():
+    """HBM bytes per launch of the head GEMV from the committed counter passes
+    (profiles/gemv_head_traffic.json), or None when the kernel sources have
+    changed since the counters were taken (the record carries their hash)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemv_head_traffic.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for fn in rec["sources"]:
+            h.update(open(os.path.join(ROOT, "block_quantized_matmul_02_amd", "csrc", fn), "rb").read())
+        return int(rec["traffic_bytes"]) if h.hexdigest() == rec["sources_sha256"] else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def timed_loop(torch, stream, steps, fns):
     """Time ``steps`` passes of ``fns`` (a list of (name, callable)).
 
@@ -141,9 +157,9 @@ def main():
             "ms_per_step": round(ms_step, 5),
             "config": {"workload": "decode head GEMV: m=1, K=4096, N=64448, Q8_0 weights, q8_1 activations",
                        "m": m, "k": k, "n": n, "weight_copies_rotated": ROTATE, "parallelism": "none"},
-            "roofline": {"bound": "hbm", "kernel": "q8_0_gemv_kernel<1>", "achieved": round(achieved, 1),
+            "roofline": {"bound": "hbm", "kernel": "q8_0_gemv_kernel<1, false>", "achieved": round(achieved, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": None, "bytes_per_launch": gemv_bytes,
+                         "traffic": recorded_traffic(), "bytes_per_launch": gemv_bytes,
                          "avg_launch_us": round(per["gemv"] * 1e3, 3)},
             "steps_detail_us": {k2: round(v * 1e3, 3) for k2, v in per.items()},
         })
