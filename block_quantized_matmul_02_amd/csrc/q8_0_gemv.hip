@@ -36,9 +36,9 @@ namespace bqm {
 
 constexpr int kGemvThreads = 256;      // 4 waves, each streaming its own tiles
 constexpr int kGemvWaves = kGemvThreads / 64;
-constexpr int kSlots = 9;              // 9 x 1 KiB per tile (2 rows of K=4096, 8.5 KiB)
+constexpr int kSlots = 5;              // 5 x 1 KiB of loads per tile (one row of K=4096, 4352 B)
 constexpr int kTileBytes = kSlots * 1024;
-constexpr int kMaxPairsPerSeg = 180;   // 180 * 68 = 12240 bytes <= one tile
+constexpr int kMaxPairsPerSeg = 72;    // 72 * 68 = 4896 bytes <= one tile
 constexpr int kActLdsMax = 98304;      // activation bytes staged per workgroup
 // Cache policy of the weight loads: non-temporal.  Every weight byte is read
 // exactly once, so keeping it out of the caches frees them for the activations
@@ -58,6 +58,7 @@ struct GemvGeom {
     int RS;        // row-steps per tile = RT / G
     int CPS;       // 16-byte chunks per row segment = 68*PS/16
     int TC;        // chunks per tile = RT * CPS
+    int TB;        // LDS bytes of one staged tile = 16 * TC
     int n_row_tiles;
 };
 
@@ -83,7 +84,9 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     // resource) is then wave-uniform and lives in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    uint8_t *tile = lds + act_bytes + wave * kTileBytes;
+    // two staged tiles per wave, back to back
+    uint8_t *tile0 = lds + act_bytes + wave * 2 * g.TB;
+    uint8_t *tile1 = tile0 + g.TB;
 
     // Activations (int8 quants and d_x) are staged once per workgroup, after
     // the first weight tiles are in flight so HBM starts streaming at once.
@@ -136,12 +139,13 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         for (int s = 0; s < kSlots; s++) buf[s] = buf_load16(rs, voff[s]);
     };
 
-    auto stage = [&](const u32x4 (&buf)[kSlots]) {
+    auto stage = [&](const u32x4 (&buf)[kSlots], uint8_t *tl) {
         // Wave-private buffer; LDS accesses of one wave complete in order, so the
-        // previous tile's reads are done before these writes land.
+        // previous tile's reads are done before these writes land.  Chunks past
+        // the tile (zeros) are not written.
 #pragma unroll
         for (int s = 0; s < kSlots; s++)
-            *reinterpret_cast<u32x4 *>(tile + 1024 * s + 16 * lane) = buf[s];
+            if (64 * s + lane < g.TC) *reinterpret_cast<u32x4 *>(tl + 1024 * s + 16 * lane) = buf[s];
     };
 
     const int li = lane & (g.L - 1);     // lane index inside its row
@@ -175,8 +179,8 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     // One pair (two blocks) of tile row rl, pair pl of the segment, for every
     // token: a[t] += d_w*d_x*S for both blocks.  The activation operands come
     // from LDS, or from xr when the lane's pair is the same for every row.
-    auto pair_dot = [&](int rl, int pl, int sg, float (&a)[M], const ActPair *xr) {
-        const uint32_t *pw = reinterpret_cast<const uint32_t *>(tile + rl * (68 * g.PS) + 68 * pl);
+    auto pair_dot = [&](const uint8_t *tl, int rl, int pl, int sg, float (&a)[M], const ActPair *xr) {
+        const uint32_t *pw = reinterpret_cast<const uint32_t *>(tl + rl * (68 * g.PS) + 68 * pl);
         uint32_t dw[17];
 #pragma unroll
         for (int d = 0; d < 17; d++) dw[d] = pw[d];
@@ -223,48 +227,21 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         }
     };
 
-    auto compute = [&](int q) {
+    // Work item q, staged in tile tl.
+    auto compute = [&](int q, const uint8_t *tl) {
         const int rt = wid + nwaves * (q / g.nseg);
         const int sg = q - (q / g.nseg) * g.nseg;
         const int row0 = rt * g.RT;
-        if (M <= 2 && g.nseg == 1 && g.J == 1) {
-            // Whole rows with one pair per lane (K <= 4096): the lane's pair,
-            // and so its activation operands, are the same for every row; they
-            // sit in registers.  Two row-steps at a time as two independent
-            // chains, so the LDS and dot-product latencies of one overlap the
-            // other's.
-            int rs = 0;
-            for (; rs + 1 < g.RS; rs += 2) {
-                const int rl0 = rs * g.G + gr, rl1 = rl0 + g.G;
-                float a0[M], a1[M];
-#pragma unroll
-                for (int t = 0; t < M; t++) a0[t] = a1[t] = 0.0f;
-                if (li < g.PS) {
-                    pair_dot(rl0, li, 0, a0, xreg);
-                    pair_dot(rl1, li, 0, a1, xreg);
-                }
-                reduce_store(a0, row0 + rl0);
-                reduce_store(a1, row0 + rl1);
-            }
-            if (rs < g.RS) {
-                const int rl = rs * g.G + gr;
-                float a0[M];
-#pragma unroll
-                for (int t = 0; t < M; t++) a0[t] = 0.0f;
-                if (li < g.PS) pair_dot(rl, li, 0, a0, xreg);
-                reduce_store(a0, row0 + rl);
-            }
-        } else if (g.nseg == 1) {
-            // Whole rows, activation operands read from LDS.
-            int rs = 0;
-            for (; rs < g.RS; rs++) {
+        if (g.nseg == 1) {
+            // Whole rows.
+            for (int rs = 0; rs < g.RS; rs++) {
                 const int rl = rs * g.G + gr;
                 float a0[M];
 #pragma unroll
                 for (int t = 0; t < M; t++) a0[t] = 0.0f;
                 for (int j = 0; j < g.J; j++) {
                     const int pl = li + g.L * j;
-                    if (pl < g.PS) pair_dot(rl, pl, 0, a0, nullptr);
+                    if (pl < g.PS) pair_dot(tl, rl, pl, 0, a0, nullptr);
                 }
                 reduce_store(a0, row0 + rl);
             }
@@ -277,14 +254,37 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
             }
             for (int j = 0; j < g.J; j++) {
                 const int pl = li + g.L * j;
-                if (pl < g.PS) pair_dot(gr, pl, sg, acc, nullptr);
+                if (pl < g.PS) pair_dot(tl, gr, pl, sg, acc, nullptr);
             }
             if (sg == g.nseg - 1) reduce_store(acc, row0 + gr);
         }
     };
 
+    // Items q (tile t0) and q+1 (tile t1, present when two) when every row
+    // gives a lane the same pair (whole rows, one pair per lane: K <= 4096)
+    // and m <= 2: the activation operands sit in registers, and the two tiles
+    // run as two independent chains so the LDS and dot-product latencies of
+    // one overlap the other's.
+    const bool fast = M <= 2 && g.nseg == 1 && g.J == 1;
+    auto compute_pair_fast = [&](int q, const uint8_t *t0, const uint8_t *t1, bool two) {
+        const int row0 = (wid + nwaves * q) * g.RT;
+        const int row1 = (wid + nwaves * (q + 1)) * g.RT;
+        for (int rs = 0; rs < g.RS; rs++) {
+            const int rl = rs * g.G + gr;
+            float a0[M], a1[M];
+#pragma unroll
+            for (int t = 0; t < M; t++) a0[t] = a1[t] = 0.0f;
+            if (li < g.PS) {
+                pair_dot(t0, rl, li, 0, a0, xreg);
+                pair_dot(t1, rl, li, 0, a1, xreg);
+            }
+            reduce_store(a0, row0 + rl);
+            if (two) reduce_store(a1, row1 + rl);
+        }
+    };
+
     auto load_xreg = [&]() {
-        if (M <= 2 && g.nseg == 1 && g.J == 1 && li < g.PS) {
+        if (fast && li < g.PS) {
 #pragma unroll
             for (int t = 0; t < (M <= 2 ? M : 1); t++) xreg[t] = load_act(t, li);
         }
@@ -298,34 +298,44 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         stage_activations();
         load_xreg();
         if (Q == 1) {
-            stage(bufA);
-            compute(0);
+            stage(bufA, tile0);
+            if (fast) compute_pair_fast(0, tile0, tile0, false);
+            else compute(0, tile0);
         }
         return;
     }
-    // Two items in flight.  Every fill is issued unconditionally (a refill
-    // past the last item is empty), so the compiler knows that the other
-    // buffer's loads are still in flight when a buffer is staged and waits
-    // only for the older loads; a fill behind a branch would make it wait for
-    // all of them.  The last one or two items are drained after the loop.
+    // Two items in flight, each staged into its own LDS tile before either is
+    // computed, so both refills are issued before the arithmetic starts and no
+    // buffer sits idle behind it.  Every fill in the loop is issued
+    // unconditionally (a refill past the last item is empty), so the compiler
+    // knows that the other buffer's loads are still in flight when a buffer is
+    // staged and waits only for the older loads; a fill behind a branch would
+    // make it wait for all of them.  The last one or two items are drained
+    // after the loop.
     issue(bufA, 0);
     issue(bufB, 1);
     stage_activations();
     load_xreg();
     int q = 0;
     for (; q + 2 < Q; q += 2) {
-        stage(bufA);
+        stage(bufA, tile0);
         issue(bufA, q + 2);
-        compute(q);
-        stage(bufB);
+        stage(bufB, tile1);
         issue(bufB, q + 3);
-        compute(q + 1);
+        if (fast) {
+            compute_pair_fast(q, tile0, tile1, true);
+        } else {
+            compute(q, tile0);
+            compute(q + 1, tile1);
+        }
     }
-    stage(bufA);
-    compute(q);
-    if (q + 1 < Q) {
-        stage(bufB);
-        compute(q + 1);
+    stage(bufA, tile0);
+    stage(bufB, tile1);
+    if (fast) {
+        compute_pair_fast(q, tile0, tile1, q + 1 < Q);
+    } else {
+        compute(q, tile0);
+        if (q + 1 < Q) compute(q + 1, tile1);
     }
 }
 
@@ -356,6 +366,7 @@ static bool make_geom(int k, int n, int64_t w_row_bytes, GemvGeom &g) {
     }
     g.RS = g.RT / g.G;
     g.TC = g.RT * g.CPS;
+    g.TB = 16 * g.TC;
     if (g.TC > kSlots * 64) return false;
     g.n_row_tiles = (n + g.RT - 1) / g.RT;
     (void)w_row_bytes;
@@ -367,7 +378,7 @@ static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, 
                        int k, int n, const GemvGeom &g, hipStream_t stream) {
     const int nb = k / kQK;
     const int act_bytes = (M * k + M * nb * 4 + 15) & ~15;
-    const int lds_bytes = act_bytes + kGemvWaves * kTileBytes;
+    const int lds_bytes = act_bytes + kGemvWaves * 2 * g.TB;
     static int attr_done = 0;
     if (!attr_done) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false>),
