@@ -71,7 +71,12 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kWeightLoadPolicy));
 }
 
-template <int M, bool SINGLE>
+// Activation chunks a thread can hold in registers while the first weight
+// tiles are issued (PRE variants): up to 2 x 256 chunks of 16 bytes, m*k <= 8192.
+constexpr int kActPre = 2;
+
+// PRE = activation chunks per thread loaded ahead of the tiles (0 = none).
+template <int M, bool SINGLE, int PRE>
 __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     const uint8_t *__restrict__ w, int64_t w_row_bytes, const int8_t *__restrict__ xq,
     const float *__restrict__ xds, float *__restrict__ y, int k, int n, GemvGeom g) {
@@ -90,6 +95,41 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
 
     // Activations (int8 quants and d_x) are staged once per workgroup, after
     // the first weight tiles are in flight so HBM starts streaming at once.
+    // Plain loads issued after the tiles' loads can only be waited for
+    // together with them, so the first arithmetic would wait for every
+    // tile of the first wave of requests.  The PRE variants (m*k <= 8192,
+    // m*k/32 <= 256) therefore issues its activation loads into registers
+    // before the tiles' loads and waits for those alone.
+    const __amdgpu_buffer_rsrc_t rxq = make_rsrc(xq, (uint32_t)(M * k));
+    const __amdgpu_buffer_rsrc_t rxd = make_rsrc(xds, (uint32_t)(M * nb * 8));
+    u32x4 pre_q[PRE > 0 ? PRE : 1];
+    float pre_d;
+    auto preload_activations = [&]() {
+#pragma unroll
+        for (int i = 0; i < PRE; i++)
+            pre_q[i] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rxq, (uint32_t)(threadIdx.x + kGemvThreads * i) * 16u, 0, 0));
+        pre_d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxd, threadIdx.x * 8u, 0, 0));
+    };
+    // Every preloaded value is stored unconditionally (values past the
+    // activations go to this wave's first tile, which is overwritten before
+    // it is read): a store behind a branch lets the compiler sink its load
+    // into the branch, behind the tiles' loads.
+    auto store_preloaded = [&]() {
+        const int chunks = M * k / 16;
+#pragma unroll
+        for (int i = 0; i < PRE; i++) {
+            const int c = threadIdx.x + kGemvThreads * i;
+            const int t = c / (k / 16);
+            const int cc = c - t * (k / 16);
+            const int p = cc >> 2, ci = cc & 3;
+            uint8_t *dst = c < chunks ? act_q + t * k + 64 * p + 16 * ((ci + (p >> 1)) & 3) : tile0 + 16 * lane;
+            *reinterpret_cast<u32x4 *>(dst) = pre_q[i];
+        }
+        float *dd = (int)threadIdx.x < M * nb ? act_d + threadIdx.x : reinterpret_cast<float *>(tile0) + lane;
+        *dd = pre_d;
+        __syncthreads();
+    };
     auto stage_activations = [&]() {
         const int chunks = M * k / 16;
         for (int c = threadIdx.x; c < chunks; c += kGemvThreads) {
@@ -294,8 +334,10 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     if (SINGLE) {
         // Launched with at most one item per wave: no pipeline (every wave
         // still stages the activations, which ends in a workgroup barrier).
+        if (PRE) preload_activations();
         if (Q == 1) issue(bufA, 0);
-        stage_activations();
+        if (PRE) store_preloaded();
+        else stage_activations();
         load_xreg();
         if (Q == 1) {
             stage(bufA, tile0);
@@ -312,9 +354,11 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     // staged and waits only for the older loads; a fill behind a branch would
     // make it wait for all of them.  The last one or two items are drained
     // after the loop.
+    if (PRE) preload_activations();
     issue(bufA, 0);
     issue(bufB, 1);
-    stage_activations();
+    if (PRE) store_preloaded();
+    else stage_activations();
     load_xreg();
     int q = 0;
     for (; q + 2 < Q; q += 2) {
@@ -373,22 +417,27 @@ static bool make_geom(int k, int n, int64_t w_row_bytes, GemvGeom &g) {
     return true;
 }
 
+template <int M, bool SINGLE, int PRE>
+static int launch_variant(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y,
+                          int k, int n, const GemvGeom &g, int grid, int lds_bytes, hipStream_t stream) {
+    static int attr_done = 0;
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, SINGLE, PRE>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
+        attr_done = 1;
+    }
+    hipLaunchKernelGGL((q8_0_gemv_kernel<M, SINGLE, PRE>), dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w,
+                       w_row_bytes, xq, xds, y, k, n, g);
+    return launch_status();
+}
+
 template <int M>
 static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y,
                        int k, int n, const GemvGeom &g, hipStream_t stream) {
     const int nb = k / kQK;
     const int act_bytes = (M * k + M * nb * 4 + 15) & ~15;
     const int lds_bytes = act_bytes + kGemvWaves * 2 * g.TB;
-    static int attr_done = 0;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, true>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
-        attr_done = 1;
-    }
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     int per_cu = (160 * 1024) / lds_bytes;
@@ -399,13 +448,20 @@ static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, 
     if (want < grid) grid = want;
     // every wave holds at most one item: the variant without the pipeline
     const bool single = (int64_t)g.n_row_tiles * g.nseg <= (int64_t)grid * kGemvWaves;
-    if (single)
-        hipLaunchKernelGGL((q8_0_gemv_kernel<M, true>), dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w,
-                           w_row_bytes, xq, xds, y, k, n, g);
-    else
-        hipLaunchKernelGGL((q8_0_gemv_kernel<M, false>), dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w,
-                           w_row_bytes, xq, xds, y, k, n, g);
-    return launch_status();
+    // the activations fit in the registers of the workgroup's threads
+    // (PRE variants are built for m <= 2, the decode sizes)
+    const int pre_chunks = (M * k / 16 + kGemvThreads - 1) / kGemvThreads;
+    const bool pre = M <= 2 && pre_chunks <= kActPre && M * nb <= kGemvThreads;
+    if (pre && pre_chunks == 1) {
+        if (single) return launch_variant<M, true, (M <= 2 ? 1 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
+        return launch_variant<M, false, (M <= 2 ? 1 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
+    }
+    if (pre) {
+        if (single) return launch_variant<M, true, (M <= 2 ? 2 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
+        return launch_variant<M, false, (M <= 2 ? 2 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
+    }
+    if (single) return launch_variant<M, true, 0>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
+    return launch_variant<M, false, 0>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
 }
 
 }  // namespace bqm
