@@ -62,30 +62,39 @@ def recorded_traffic():
 def timed_loop(torch, stream, steps, fns):
     """Time ``steps`` passes of ``fns`` (a list of (name, callable)).
 
-    The step time comes from events around the whole loop, with nothing added
-    between calls.  Each callable's duration comes from a second loop per
-    callable that launches it ``steps`` times back to back between two events
-    on the launch stream (so per-event overhead is amortized; the inter-launch
-    gap stays in, which errs on the slow side).
+    The launches are captured once into a HIP graph (torch.cuda.graph) and
+    replayed, so host-side launch overhead is out of the measurement: the
+    kernels run back to back as they would inside an engine's decode step.
+    The step time comes from events on the replay stream around one replay of
+    the ``steps`` passes.  Each callable's duration comes from a second graph
+    that launches it ``steps`` times back to back, timed the same way.
     Returns (total ms of the step loop, {name: mean ms per call})."""
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(steps):
-        for _, fn in fns:
-            fn(s)
-    end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    per = {}
-    for name, fn in fns:
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for s in range(steps):
-            fn(s)
-        b.record(stream)
+    def capture(calls):
+        for s in range(2):                # first calls outside capture (one-time setup)
+            for fn in calls:
+                fn(s)
         torch.cuda.synchronize()
-        per[name] = a.elapsed_time(b) / steps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(steps):
+                for fn in calls:
+                    fn(s)
+        torch.cuda.synchronize()
+        return g
+
+    def replay_ms(g):
+        rs = torch.cuda.current_stream()
+        g.replay()                          # warm replay
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(rs)
+        g.replay()
+        b.record(rs)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    total_ms = replay_ms(capture([fn for _, fn in fns]))
+    per = {name: replay_ms(capture([fn])) / steps for name, fn in fns}
     return total_ms, per
 
 
