@@ -54,6 +54,8 @@ def _load():
         lib.oracle_e4m3_quantize_amax.argtypes = [P, P, P, ctypes.c_float, I, I]
         lib.oracle_e4m3_matmul.argtypes = [P, P, P, I, I, I, P, P]
         lib.oracle_e4m3_matmul_sampled.argtypes = [P, P, P, I, I, P, P, P, P]
+        lib.oracle_e4m3_gemv.argtypes = [P, P, ctypes.c_float, I, I, I, P, P]
+        lib.oracle_e4m3_gemv_sampled.argtypes = [P, P, ctypes.c_float, I, I, P, P, P, P]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -168,4 +170,29 @@ def e4m3_matmul_sampled(w, xq, scales, tok, row):
     T = np.empty(len(tok), dtype=np.float64)
     _load().oracle_e4m3_matmul_sampled(_p(w), _p(xq), _p(scales), w.shape[1], len(tok),
                                        _p(tok), _p(row), _p(y), _p(T))
+    return y, T
+
+
+def e4m3_gemv(w: np.ndarray, x: np.ndarray, w_scale: float):
+    """Decode GEMV on raw e4m3 weights: y = w_scale * x @ dec(w)^T in fp64,
+    x used as f32.  Returns (y [m, n], sum|terms| [m, n])."""
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32)
+    n, k = w.shape
+    m = x.shape[0]
+    y = np.empty((m, n), dtype=np.float64)
+    T = np.empty((m, n), dtype=np.float64)
+    _load().oracle_e4m3_gemv(_p(w), _p(x), ctypes.c_float(w_scale), m, k, n, _p(y), _p(T))
+    return y, T
+
+
+def e4m3_gemv_sampled(w, x, w_scale, tok, row):
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32)
+    tok = _c(tok, np.int64)
+    row = _c(row, np.int64)
+    y = np.empty(len(tok), dtype=np.float64)
+    T = np.empty(len(tok), dtype=np.float64)
+    _load().oracle_e4m3_gemv_sampled(_p(w), _p(x), ctypes.c_float(w_scale), w.shape[1], len(tok),
+                                     _p(tok), _p(row), _p(y), _p(T))
     return y, T

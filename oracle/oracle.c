@@ -304,3 +304,42 @@ void oracle_e4m3_matmul_sampled(const uint8_t *w, const uint8_t *xq, const float
     for (int64_t p = 0; p < npairs; p++)
         e4m3_dot(w + row[p] * k, xq + tok[p] * k, k, folded, &y[p], &tabs[p]);
 }
+
+/*
+ * e4m3 decode GEMV on raw e4m3 weights with a per-tensor scale:
+ * y[t][n] = w_scale * sum_k x[t][k] * dec(w[n][k]), the activation used as
+ * the f32 values it is (the pages name the decode kernel, qmatvec_e4m3_mmvq,
+ * and its per-tensor scalar-scale weight class, "fp8_ffi.rs" st_e4m3_enabled
+ * doc, but not its activation format; the plainest reading is the f32
+ * activation against the decoded weights).  Accumulated in fp64, so the
+ * result is within ~1e-12 relative of the exact sum; tabs is the fp64
+ * sum of |terms| times |w_scale|.
+ */
+static void e4m3_gemv_dot(const uint8_t *wrow, const float *xrow, int64_t k, double ws, double *y,
+                          double *tabs) {
+    double acc = 0.0, aabs = 0.0;
+    for (int64_t i = 0; i < k; i++) {
+        double p = (double)xrow[i] * e4m3_table[wrow[i]];
+        acc += p;
+        aabs += fabs(p);
+    }
+    *y = ws * acc;
+    *tabs = fabs(ws) * aabs;
+}
+
+void oracle_e4m3_gemv(const uint8_t *w, const float *x, float w_scale, int64_t m, int64_t k, int64_t n,
+                      double *y, double *tabs) {
+    e4m3_fill_table();
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t t = 0; t < m; t++)
+            e4m3_gemv_dot(w + r * k, x + t * k, k, (double)w_scale, &y[t * n + r], &tabs[t * n + r]);
+}
+
+void oracle_e4m3_gemv_sampled(const uint8_t *w, const float *x, float w_scale, int64_t k, int64_t npairs,
+                              const int64_t *tok, const int64_t *row, double *y, double *tabs) {
+    e4m3_fill_table();
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npairs; p++)
+        e4m3_gemv_dot(w + row[p] * k, x + tok[p] * k, k, (double)w_scale, &y[p], &tabs[p]);
+}

@@ -376,3 +376,65 @@ def test_e4m3_matmul_one_hot_and_fp64_reference():
     tok = np.array([4, 0, 2]); row = np.array([12, 3, 0])
     ys, Ts = oracle.e4m3_matmul_sampled(codes, xq, sc, tok, row)
     assert np.array_equal(ys, y[tok, row]) and np.array_equal(Ts, T[tok, row])
+
+
+# --------------------------------------------------------------------------- e4m3 decode GEMV
+
+
+@pytest.mark.parametrize("code,v", [(0x38, 1.0), (0x01, -3.25), (0x7E, 0.0078125), (0xC5, 1.5), (0x80, 7.0)])
+def test_e4m3_gemv_closed_form_constant_inputs(code, v):
+    # every weight the same code, every activation the same value:
+    # y = w_scale * K * v * dec(code), an exact product here
+    k, n, ws = 512, 3, 0.375
+    w = np.full((n, k), code, np.uint8)
+    x = np.full((2, k), v, np.float32)
+    y, T = oracle.e4m3_gemv(w, x, ws)
+    d = float(_torch_decode([code])[0])
+    assert np.all(y == ws * k * v * d)
+    assert np.all(T == abs(ws * k * v * d))
+
+
+def test_e4m3_gemv_one_hot_picks_column_and_row():
+    rng = np.random.default_rng(31)
+    n, k = 37, 256
+    codes, ws = workloads.e4m3_weights(n, k, rng)
+    x = np.zeros((3, k), np.float32)
+    x[0, 5] = 1.0
+    x[1, 200] = -2.0
+    x[2, 255] = 0.5
+    y, _ = oracle.e4m3_gemv(codes, x, ws)
+    dec = _torch_decode(codes).astype(np.float64)
+    assert np.array_equal(y[0], dec[:, 5] * ws)
+    assert np.array_equal(y[1], -2.0 * dec[:, 200] * ws)
+    assert np.array_equal(y[2], 0.5 * dec[:, 255] * ws)
+
+
+def test_e4m3_gemv_matches_fp64_matmul_of_torch_decoded_weights():
+    rng = np.random.default_rng(32)
+    n, k, m = 64, 1280, 9
+    codes, ws = workloads.e4m3_weights(n, k, rng)
+    x = workloads.activations(m, k, rng, outliers=True)
+    y, T = oracle.e4m3_gemv(codes, x, ws)
+    dec = _torch_decode(codes).astype(np.float64)
+    ref = float(ws) * (x.astype(np.float64) @ dec.T)
+    tref = abs(float(ws)) * (np.abs(x.astype(np.float64)) @ np.abs(dec).T)
+    assert np.all(np.abs(y - ref) <= 1e-12 * tref)
+    assert np.allclose(T, tref, rtol=1e-12, atol=0)
+    ys, Ts = oracle.e4m3_gemv_sampled(codes, x, ws, np.array([0, 8, 4]), np.array([63, 0, 17]))
+    assert np.array_equal(ys, y[[0, 8, 4], [63, 0, 17]])
+    assert np.array_equal(Ts, T[[0, 8, 4], [63, 0, 17]])
+
+
+def test_e4m3_gemv_tiny_brute_force_in_exact_rationals():
+    rng = np.random.default_rng(33)
+    n, k, m = 3, 7, 2
+    codes = rng.integers(0, 256, size=(n, k)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x12          # no NaN codes
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    ws = np.float32(0.0123)
+    y, _ = oracle.e4m3_gemv(codes, x, float(ws))
+    dec = _torch_decode(codes)
+    for t in range(m):
+        for r in range(n):
+            exact = Fraction(float(ws)) * sum(Fraction(float(x[t, i])) * Fraction(float(dec[r, i])) for i in range(k))
+            assert abs(Fraction(y[t, r]) - exact) <= abs(exact) * Fraction(1, 2**50) + Fraction(1, 2**1000)
