@@ -19,6 +19,7 @@ BQM_EINVAL = 1
 BQM_EUNSUPPORTED = 2
 BQM_EHIP_BASE = 10000
 GEMV_MAX_M = 15
+E4M3_GEMV_MAX_M = 16
 
 _lib = None
 
@@ -43,8 +44,9 @@ def lib() -> ctypes.CDLL:
         L.bqm_q8_0_gemm.argtypes = [P, I64, P, P, P, I, I, I, P]
         L.bqm_e4m3_quantize_amax.argtypes = [P, P, P, F, I, I, P]
         L.bqm_e4m3_gemm.argtypes = [P, P, P, P, I, I, I, P]
+        L.bqm_e4m3_gemv.argtypes = [P, P, F, P, I, I, I, P]
         for fn in ("bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax",
-                   "bqm_e4m3_gemm"):
+                   "bqm_e4m3_gemm", "bqm_e4m3_gemv"):
             getattr(L, fn).restype = ctypes.c_int
         L.bqm_strerror.argtypes = [I]
         L.bqm_strerror.restype = ctypes.c_char_p
@@ -164,4 +166,21 @@ def bqm_e4m3_gemm(w, xq, scales, y=None):
     _check(y, torch.float32, "y", (m, n))
     rc = lib().bqm_e4m3_gemm(_ptr(w), _ptr(xq), _ptr(scales), _ptr(y), m, k, n, _stream(w))
     _raise("bqm_e4m3_gemm", rc)
+    return y
+
+
+def bqm_e4m3_gemv(w, x, w_scale: float, y=None):
+    """e4m3 decode GEMV, 1 <= m <= 16: codes ``w [n, k]`` against f32 ``x [m, k]`` -> f32 ``y [m, n]``
+    = w_scale * x @ dec(w)^T."""
+    import torch
+
+    n, k = w.shape
+    m = x.shape[0]
+    _check(w, torch.uint8, "w")
+    _check(x, torch.float32, "x", (m, k))
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _check(y, torch.float32, "y", (m, n))
+    rc = lib().bqm_e4m3_gemv(_ptr(w), _ptr(x), ctypes.c_float(w_scale), _ptr(y), m, k, n, _stream(w))
+    _raise("bqm_e4m3_gemv", rc)
     return y

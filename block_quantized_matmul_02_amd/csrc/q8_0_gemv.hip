@@ -432,6 +432,24 @@ static int launch_variant(const uint8_t *w, int64_t w_row_bytes, const int8_t *x
     return launch_status();
 }
 
+// Resident workgroups per CU of the pipelined variant (registers and LDS),
+// at most 4.
+template <int M, int PRE>
+static int gemv_per_cu(int lds_bytes) {
+    static int attr_done = 0;   // allow up to 160 KiB of LDS before asking
+    if (!attr_done) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+            return 1;
+        attr_done = 1;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE>),
+                                                     kGemvThreads, lds_bytes) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    return per_cu > 4 ? 4 : per_cu;
+}
+
 template <int M>
 static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y,
                        int k, int n, const GemvGeom &g, hipStream_t stream) {
@@ -440,23 +458,23 @@ static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, 
     const int lds_bytes = act_bytes + kGemvWaves * 2 * g.TB;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    int per_cu = (160 * 1024) / lds_bytes;
-    if (per_cu < 1) per_cu = 1;
-    if (per_cu > 4) per_cu = 4;
+    // the activations fit in the registers of the workgroup's threads
+    // (PRE variants are built for m <= 2, the decode sizes)
+    const int pre_chunks = (M * k / 16 + kGemvThreads - 1) / kGemvThreads;
+    const int pre = (M <= 2 && pre_chunks <= kActPre && M * nb <= kGemvThreads) ? pre_chunks : 0;
+    const int per_cu = pre == 1   ? gemv_per_cu<M, (M <= 2 ? 1 : 0)>(lds_bytes)
+                       : pre == 2 ? gemv_per_cu<M, (M <= 2 ? 2 : 0)>(lds_bytes)
+                                  : gemv_per_cu<M, 0>(lds_bytes);
     int want = (g.n_row_tiles + kGemvWaves - 1) / kGemvWaves;
     int grid = cus * per_cu;
     if (want < grid) grid = want;
     // every wave holds at most one item: the variant without the pipeline
     const bool single = (int64_t)g.n_row_tiles * g.nseg <= (int64_t)grid * kGemvWaves;
-    // the activations fit in the registers of the workgroup's threads
-    // (PRE variants are built for m <= 2, the decode sizes)
-    const int pre_chunks = (M * k / 16 + kGemvThreads - 1) / kGemvThreads;
-    const bool pre = M <= 2 && pre_chunks <= kActPre && M * nb <= kGemvThreads;
-    if (pre && pre_chunks == 1) {
+    if (pre == 1) {
         if (single) return launch_variant<M, true, (M <= 2 ? 1 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
         return launch_variant<M, false, (M <= 2 ? 1 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
     }
-    if (pre) {
+    if (pre == 2) {
         if (single) return launch_variant<M, true, (M <= 2 ? 2 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
         return launch_variant<M, false, (M <= 2 ? 2 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
     }

@@ -49,6 +49,8 @@ extern "C" {
  * "fp8_ffi.rs" module doc: decode and the m<=9 verify tier stay on the GEMV;
  * prefill m>=16 moves to the GEMM). */
 #define BQM_GEMV_MAX_M 15
+/* Largest m the e4m3 decode GEMV accepts. */
+#define BQM_E4M3_GEMV_MAX_M 16
 
 /*
  * q8_1 activation quantization, per token and 32-value block
@@ -135,6 +137,27 @@ int bqm_e4m3_quantize_amax(const float *x, uint8_t *xq, float *scales, float w_s
  */
 int bqm_e4m3_gemm(const uint8_t *w, const uint8_t *xq, const float *scales, float *y, int m,
                   int k, int n, void *stream);
+
+/*
+ * e4m3 decode GEMV on raw e4m3 weights with a per-tensor scale ("fp8_ffi.rs"
+ * st_e4m3_enabled doc: decode reads the checkpoint's own e4m3 bytes through
+ * qmatvec_e4m3_mmvq, for the per-tensor scalar-scale class).  The pages do
+ * not give that kernel's activation format; here the activation is the f32
+ * values themselves.
+ *
+ *   w       : uint8 E4M3FN codes [n][k] (row-major, k bytes per row),
+ *             16-byte aligned.
+ *   x       : f32 [m][k] activations, 16-byte aligned.
+ *   w_scale : the per-tensor f32 weight scale (a host value).
+ *   y       : f32 [m][n] out, 4-byte aligned, fully overwritten.
+ *   1 <= m <= BQM_E4M3_GEMV_MAX_M, n >= 1, k >= 256, w_scale finite (else
+ *   BQM_EINVAL);
+ *   k % 256 == 0 and k <= 8192 (else BQM_EUNSUPPORTED).  Codes with magnitude
+ *   0x7F are NaN; callers must not pass them.
+ * y[t][r] = w_scale * sum_k x[t][k] * dec(w[r][k]), f32 accumulation.
+ */
+int bqm_e4m3_gemv(const uint8_t *w, const float *x, float w_scale, float *y, int m, int k, int n,
+                  void *stream);
 
 /* Text for a return code; never NULL, static storage. */
 const char *bqm_strerror(int rc);

@@ -29,10 +29,10 @@ def declared_symbols():
     return sorted(set(re.findall(r"\b(bqm_\w+)\s*\(", text)))
 
 
-def test_header_declares_the_five_calls_and_strerror():
+def test_header_declares_the_calls_and_strerror():
     assert declared_symbols() == sorted([
         "bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax", "bqm_e4m3_gemm",
-        "bqm_strerror"])
+        "bqm_e4m3_gemv", "bqm_strerror"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -113,6 +113,25 @@ def test_e4m3_validation(L):
     assert g(A16, B16, C16, D16, 1, 128, 0, NUL) == 1
     assert g(A16, B16, C16, D16, 1, 192, 8, NUL) == 2                  # k % 128
     assert g(A16, MIS2, C16, D16, 1, 128, 8, NUL) == 2
+
+
+def test_e4m3_gemv_validation(L):
+    f = L.bqm_e4m3_gemv
+    F = ctypes.c_float
+    assert f(NUL, B16, F(1.0), D16, 1, 4096, 8, NUL) == 1
+    assert f(A16, NUL, F(1.0), D16, 1, 4096, 8, NUL) == 1
+    assert f(A16, B16, F(1.0), NUL, 1, 4096, 8, NUL) == 1
+    assert f(A16, B16, F(1.0), D16, 0, 4096, 8, NUL) == 1
+    assert f(A16, B16, F(1.0), D16, 17, 4096, 8, NUL) == 1             # m > 16
+    assert f(A16, B16, F(1.0), D16, 1, 128, 8, NUL) == 1               # k < 256
+    assert f(A16, B16, F(1.0), D16, 1, 4096, 0, NUL) == 1
+    assert f(A16, B16, F(float("nan")), D16, 1, 4096, 8, NUL) == 1
+    assert f(A16, B16, F(float("-inf")), D16, 1, 4096, 8, NUL) == 1
+    assert f(A16, B16, F(1.0), D16, 1, 4096 + 128, 8, NUL) == 2        # k % 256
+    assert f(A16, B16, F(1.0), D16, 1, 8192 + 256, 8, NUL) == 2        # k > 8192
+    assert f(MIS2, B16, F(1.0), D16, 1, 4096, 8, NUL) == 2
+    assert f(A16, P(0x200004), F(1.0), D16, 1, 4096, 8, NUL) == 2      # x 16-byte alignment
+    assert f(A16, B16, F(1.0), P(0x400002), 1, 4096, 8, NUL) == 2
 
 
 def test_product_path_never_touches_the_oracle():
