@@ -11,7 +11,8 @@ the 256 MB Infinity Cache.
 The same JSON line also carries the prefill rows, each timed the same way:
 the m=512 MMQ GEMM (q8_1 quantize + int8 GEMM) at N in {4096, 5152, 20480}
 and the FP8-E4M3 GEMM (amax quantize + fp8 GEMM) at N=20480, with int8/fp8
-TOPS and their fraction of the matrix-core peak; a roofline object for the
+TOPS and their fraction of the matrix-core peak; the e4m3 decode GEMV
+(raw e4m3 weights, f32 activations) at m=1 and 9 on the head shape; a roofline object for the
 dominant kernel (the GEMV), measured with HIP events on the launch stream;
 and the CPU oracle timed on the host cores on a bounded sample.
 
@@ -104,7 +105,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3", "copy"], default=None,
+    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3", "e4m3_gemv", "copy"], default=None,
                     help="run one part only (for profiler passes); 'copy' runs a plain 1 GiB device copy "
                          "that calibrates the HBM byte counters")
     args = ap.parse_args()
@@ -225,6 +226,29 @@ def main():
                             "tflops": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
                             "step_tflops": round(ops / (total_ms / args.steps * 1e-3) / 1e12, 1)}
         del ws, w0, y
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- e4m3 decode GEMV
+    if args.only in (None, "e4m3_gemv"):
+        k, n = 4096, 64448
+        log("[bench] e4m3 gemv n=64448")
+        codes, w_scale = workloads.e4m3_weights(n, k, rng)
+        w0 = torch.from_numpy(codes).to(dev)
+        ws = [w0] + [w0.clone() for _ in range(ROTATE - 1)]
+        e8 = {}
+        for m in (1, 9):
+            x = torch.from_numpy(workloads.activations(m, k, rng)).to(dev)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            fns = [("gemv", lambda s: bqm.bqm_e4m3_gemv(ws[s % ROTATE], x, w_scale, y))]
+            timed_loop(torch, stream, args.warmup, fns)
+            _, per = timed_loop(torch, stream, args.steps, fns)
+            byts = n * k + m * k * 4 + m * n * 4
+            gbs = byts / (per["gemv"] * 1e-3) / 1e9
+            e8[f"m{m}"] = {"workload": f"e4m3 decode GEMV m={m}, K=4096, N=64448, raw e4m3 weights, f32 activations",
+                           "gemv_us": round(per["gemv"] * 1e3, 2), "gbs": round(gbs, 1),
+                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        out["e4m3_gemv"] = e8
+        del ws, w0
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU oracle baseline

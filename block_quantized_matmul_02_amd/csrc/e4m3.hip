@@ -20,13 +20,12 @@
 // The GEMM uses v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales
 // (E8M0 127 = 2^0): 32x32 outputs per 64-deep step, f32 accumulation, the
 // folded scale applied once in the epilogue.  Workgroup tile 128 x 64*NT
-// (4 waves of 64 x 32*NT, NT = 2..5 chosen per shape so the tiles spread
-// evenly over the CUs: m=512, N=20480 takes NT=5, 256 tiles of 128 x 320,
-// one per CU); k staged 128 at a time in double-buffered LDS with padded
-// 144-byte rows (conflict-free reads, immediate offsets), global loads one
-// stage ahead in registers, operand reads for the next 64-deep step slotted
-// between the current step's MFMAs.  Accumulators live in AGPRs (up to 160
-// per lane), leaving the VGPRs to the operand and load pipelines.
+// (8 waves of 32 x 32*NT, two waves per SIMD; NT = 2..5 chosen per shape so
+// the tiles spread evenly over the CUs: m=512, N=20480 takes NT=5, 256 tiles
+// of 128 x 320, one per CU); k staged 128 at a time in double-buffered LDS
+// with padded 144-byte rows (conflict-free reads, immediate offsets), global
+// loads one stage ahead in registers, operand reads for the next 64-deep
+// step slotted between the current step's MFMAs.
 #include "bqmm_internal.h"
 
 namespace bqm {
@@ -108,7 +107,7 @@ __global__ __launch_bounds__(256) void e4m3_quantize_kernel(const float4 *__rest
 
 constexpr int kF8BM = 128;                 // workgroup tile rows (tokens)
 constexpr int kF8KB = 128;                 // k per LDS stage (two 64-deep MFMA steps)
-constexpr int kF8Threads = 256;            // 4 waves, 2 x 2
+constexpr int kF8Threads = 512;            // 8 waves, 4 x 2: two waves per SIMD
 constexpr int kF8RowStride = kF8KB + 16;   // 144: padded LDS row (conflict-free, immediate offsets)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t f8_rsrc(const void *base, int64_t bytes) {
@@ -116,9 +115,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t f8_rsrc(const void *base, int6
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)b, 0x00020000);
 }
 
-// Workgroup tile 128 x 64*NT: 4 waves in 2 x 2, each 64 x 32*NT (2 x NT
-// 32x32 MFMA tiles).  A wave reads 2 + NT operand tiles per 64-deep step
-// for 2*NT MFMAs, so larger NT means less LDS traffic per MFMA.
+// Workgroup tile 128 x 64*NT: 8 waves in 4 x 2, each 32 x 32*NT (NT 32x32
+// MFMA tiles).  Two waves share each SIMD, so one wave's LDS reads and
+// barrier waits hide behind the other's MFMAs.  A wave reads 1 + NT operand
+// tiles per 64-deep step for NT MFMAs.
 template <int NT>
 struct F8Stage {
     uint8_t a[kF8BM * kF8RowStride];
@@ -127,8 +127,8 @@ struct F8Stage {
 
 template <int NT>
 struct F8Regs {
-    u32x4 a[4];        // 128 rows x 128 bytes = 1024 chunks, 4 per thread
-    u32x4 b[2 * NT];   // 64*NT rows x 128 bytes, 2*NT per thread
+    u32x4 a[2];        // 128 rows x 128 bytes = 1024 chunks, 2 per thread
+    u32x4 b[NT];       // 64*NT rows x 128 bytes, NT per thread
 };
 
 template <int NT>
@@ -149,52 +149,49 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
     const __amdgpu_buffer_rsrc_t rA = f8_rsrc(xq + (int64_t)m0 * k, (int64_t)(m - m0) * k);
     const __amdgpu_buffer_rsrc_t rB = f8_rsrc(w + (int64_t)n0 * k, (int64_t)(n - n0) * k);
 
-    // Thread slots: chunk q = tid + 256*s -> row q>>3 (s adds 32 rows), 16-byte
+    // Thread slots: chunk q = tid + 512*s -> row q>>3 (s adds 64 rows), 16-byte
     // chunk q&7.  The stage offset is a uniform scalar added by the load.
     const uint32_t goff = (uint32_t)((tid >> 3) * k + 16 * (tid & 7));
-    const uint32_t grow32 = (uint32_t)(32 * k);
+    const uint32_t grow64 = (uint32_t)(64 * k);
     auto load_stage = [&](F8Regs<NT> &R, int kc) {
         const int so = kc * kF8KB;
 #pragma unroll
-        for (int s = 0; s < 4; s++)
-            R.a[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, goff + s * grow32, so, 0));
+        for (int s = 0; s < 2; s++)
+            R.a[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, goff + s * grow64, so, 0));
 #pragma unroll
-        for (int s = 0; s < 2 * NT; s++)
-            R.b[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, goff + s * grow32, so, 0));
+        for (int s = 0; s < NT; s++)
+            R.b[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, goff + s * grow64, so, 0));
     };
     const int lds_off = (tid >> 3) * kF8RowStride + 16 * (tid & 7);
     auto store_stage = [&](F8Stage<NT> &S, const F8Regs<NT> &R) {
 #pragma unroll
-        for (int s = 0; s < 4; s++)
-            *reinterpret_cast<u32x4 *>(S.a + lds_off + s * 32 * kF8RowStride) = R.a[s];
+        for (int s = 0; s < 2; s++)
+            *reinterpret_cast<u32x4 *>(S.a + lds_off + s * 64 * kF8RowStride) = R.a[s];
 #pragma unroll
-        for (int s = 0; s < 2 * NT; s++)
-            *reinterpret_cast<u32x4 *>(S.b + lds_off + s * 32 * kF8RowStride) = R.b[s];
+        for (int s = 0; s < NT; s++)
+            *reinterpret_cast<u32x4 *>(S.b + lds_off + s * 64 * kF8RowStride) = R.b[s];
     };
 
-    v16f acc[2][NT];
+    v16f acc[NT];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int j = 0; j < NT; j++)
 #pragma unroll
-        for (int j = 0; j < NT; j++)
-#pragma unroll
-            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
+        for (int v = 0; v < 16; v++) acc[j][v] = 0.0f;
 
     const int khalf = lane >> 5;
     // Lane l supplies row l%32 of each 32-row operand tile and k values
     // 32*(l/32) .. +31 of the 64-deep step (the same k set for A and B).
     auto compute_stage = [&](const F8Stage<NT> &S) {
-        const uint8_t *pa = S.a + (wm * 64 + (lane & 31)) * kF8RowStride + 32 * khalf;
+        const uint8_t *pa = S.a + (wm * 32 + (lane & 31)) * kF8RowStride + 32 * khalf;
         const uint8_t *pb = S.b + (wn * 32 * NT + (lane & 31)) * kF8RowStride + 32 * khalf;
-        v8i a[2][2], b[2][NT];   // [k-step parity][tile]
+        v8i a[2], b[2][NT];   // [k-step parity][tile]
         auto ld8 = [](const uint8_t *p) {
             const u32x4 lo = *reinterpret_cast<const u32x4 *>(p);
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + 16);
             return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         };
         auto rd = [&](int ks, int slot) {
-#pragma unroll
-            for (int i = 0; i < 2; i++) a[slot][i] = ld8(pa + i * 32 * kF8RowStride + 64 * ks);
+            a[slot] = ld8(pa + 64 * ks);
 #pragma unroll
             for (int j = 0; j < NT; j++) b[slot][j] = ld8(pb + j * 32 * kF8RowStride + 64 * ks);
         };
@@ -203,11 +200,9 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
         for (int ks = 0; ks < kF8KB / 64; ks++) {
             if (ks + 1 < kF8KB / 64) rd(ks + 1, (ks + 1) & 1);
 #pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < NT; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks & 1][i], b[ks & 1][j], acc[i][j], 0, 0,
-                                                                              0, 127, 0, 127);
+            for (int j = 0; j < NT; j++)
+                acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks & 1], b[ks & 1][j], acc[j], 0, 0, 0, 127,
+                                                                       0, 127);
         }
     };
 
@@ -217,9 +212,8 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
     // the scheduling groups below can order it: global loads first, then the
     // operand reads of the first 64-deep step, then the MFMAs one at a time
     // with the second step's operand reads and then the stage stores slotted
-    // between them, so LDS latency hides behind the matrix pipe (one wave
-    // per SIMD leaves no other wave to hide it).  Masks: 0x020 VMEM read,
-    // 0x100 DS read, 0x200 DS write, 0x008 MFMA.
+    // between them.  Masks: 0x020 VMEM read, 0x100 DS read, 0x200 DS write,
+    // 0x008 MFMA.
     F8Regs<NT> R0;
     load_stage(R0, 0);
     store_stage(st[0], R0);
@@ -229,17 +223,17 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
         load_stage(R0, kc + 1);
         compute_stage(st[kc & 1]);
         store_stage(st[(kc + 1) & 1], R0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 4 + 2 * NT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 + 2 * NT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 + NT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * NT, 0);
 #pragma unroll
-        for (int r = 0; r < 2 * NT; r++) {
+        for (int r = 0; r < NT; r++) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
 #pragma unroll
-        for (int r = 0; r < 2 * NT; r++) {
+        for (int r = 0; r < NT; r++) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
         }
         __syncthreads();
     }
@@ -251,12 +245,9 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
         const int col = n0 + wn * 32 * NT + j * 32 + (lane & 31);
         if (col >= n) continue;
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-#pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
-                if (row < m) y[(int64_t)row * n + col] = acc[i][j][v] * sc;
-            }
+        for (int v = 0; v < 16; v++) {
+            const int row = m0 + wm * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+            if (row < m) y[(int64_t)row * n + col] = acc[j][v] * sc;
         }
     }
 }
