@@ -20,12 +20,13 @@
 // The GEMM uses v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales
 // (E8M0 127 = 2^0): 32x32 outputs per 64-deep step, f32 accumulation, the
 // folded scale applied once in the epilogue.  Workgroup tile 128 x 64*NT
-// (8 waves of 32 x 32*NT, two waves per SIMD; NT = 2..5 chosen per shape so
-// the tiles spread evenly over the CUs: m=512, N=20480 takes NT=5, 256 tiles
-// of 128 x 320, one per CU); k staged 128 at a time in double-buffered LDS
-// with padded 144-byte rows (conflict-free reads, immediate offsets), global
-// loads one stage ahead in registers, operand reads for the next 64-deep
-// step slotted between the current step's MFMAs.
+// (4 waves of 64 x 32*NT, NT = 2..5 chosen per shape so the tiles spread
+// evenly over the CUs: m=512, N=20480 takes NT=5, 256 tiles of 128 x 320,
+// one per CU); k staged 128 at a time in double-buffered LDS with padded
+// 144-byte rows (conflict-free reads, immediate offsets), global loads one
+// stage ahead in registers, operand reads for the next 64-deep step slotted
+// between the current step's MFMAs.  Accumulators live in AGPRs (up to 160
+// per lane), leaving the VGPRs to the operand and load pipelines.
 #include "bqmm_internal.h"
 
 namespace bqm {
@@ -206,23 +207,42 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
         }
     };
 
-    // One register copy of the next stage: its global loads are issued at the
-    // top of an iteration and written to the other LDS buffer at the bottom.
-    // The loop body is a single basic block (the last stage is peeled) so
-    // the scheduling groups below can order it: global loads first, then the
-    // operand reads of the first 64-deep step, then the MFMAs one at a time
-    // with the second step's operand reads and then the stage stores slotted
-    // between them.  Masks: 0x020 VMEM read, 0x100 DS read, 0x200 DS write,
-    // 0x008 MFMA.
-    F8Regs<NT> R0;
+    // Two register copies: the loads of stage kc+2 are issued while stage kc
+    // is computed, and written to LDS one stage later.  Past the last stage
+    // the loads re-read it (unconditional loads keep the compiler's count of
+    // loads in flight exact).  Each half-iteration is one basic block for the
+    // scheduling groups: global loads first, then the operand reads of the
+    // first 64-deep step, then the MFMAs one at a time with the second step's
+    // operand reads and then the stage stores slotted between them.  Masks:
+    // 0x020 VMEM read, 0x100 DS read, 0x200 DS write, 0x008 MFMA.
+    F8Regs<NT> R0, R1;
+    const int last = nstage - 1;
     load_stage(R0, 0);
+    load_stage(R1, min(1, last));
     store_stage(st[0], R0);
     __syncthreads();
+    int kc = 0;
 #pragma unroll 1
-    for (int kc = 0; kc + 1 < nstage; kc++) {
-        load_stage(R0, kc + 1);
-        compute_stage(st[kc & 1]);
-        store_stage(st[(kc + 1) & 1], R0);
+    for (; kc + 1 < nstage; kc += 2) {
+        load_stage(R0, min(kc + 2, last));
+        compute_stage(st[0]);
+        store_stage(st[1], R1);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 + NT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * NT, 0);
+#pragma unroll
+        for (int r = 0; r < NT; r++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < NT; r++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
+        __syncthreads();
+        load_stage(R1, min(kc + 3, last));
+        compute_stage(st[1]);
+        store_stage(st[0], R0);
         __builtin_amdgcn_sched_group_barrier(0x020, 2 + NT, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * NT, 0);
 #pragma unroll
@@ -237,7 +257,7 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
         }
         __syncthreads();
     }
-    compute_stage(st[(nstage - 1) & 1]);
+    if (kc < nstage) compute_stage(st[0]);
 
     const float sc = scales[2];
 #pragma unroll
