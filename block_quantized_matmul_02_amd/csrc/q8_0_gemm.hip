@@ -33,8 +33,6 @@
 //    lane of a half-wave reads the same four rows).
 //  * Global loads are range-checked buffer loads: ragged m and n tails read
 //    zeros (zero scales), and only in-range outputs are stored.
-#include <type_traits>
-
 #include "bqmm_internal.h"
 
 namespace bqm {
@@ -67,7 +65,7 @@ struct MmqRegs {
     u32x4 x[4];      // 4 activation chunks
     u32x4 w[4];      // one 68-byte weight block pair: dwords 0..15
     uint32_t w16;    // and dword 16
-    float dx[2];     // d_x of two blocks of one token row
+    float dx[2];     // 2 (row, block) activation scales
 };
 
 __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *__restrict__ w, int64_t w_row_bytes,
@@ -105,46 +103,29 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
     // tid>>2, pair tid&3).  dX: 2 (row q>>3, block q&7), the d of each pair.
     const int wrow = tid >> 2, wpair = tid & 3;
     const uint32_t woff = (uint32_t)(wrow * w_row_bytes + kMmqPairBytes * wpair);
-    uint32_t xoff[4];
+    uint32_t xoff[4], doff[2];
 #pragma unroll
     for (int s = 0; s < 4; s++) {
         const int q = tid + 256 * s;
         xoff[s] = (uint32_t)((q >> 4) * k + 16 * (q & 15));
     }
-    // dX: d of blocks 2*(tid&3) and +1 of row tid>>2
-    const uint32_t doff = (uint32_t)(((tid >> 2) * nb + 2 * (tid & 3)) * 8);
-    // The eleven loads of a stage, in eight parts: part b is issued while block b
-    // of the current stage is folded, so the loads trickle into the memory
-    // pipeline instead of arriving as one burst that fills the address FIFO
-    // and stalls the issuing wave.
-    auto load_part = [&](MmqRegs &R, int kc, int part) {
-        const int sx = kc * kMmqKB, sw = kc * (kMmqBlocks * kQ80Bytes), sd = kc * kMmqBlocks * 8;
-        switch (part) {
-        case 0:
-        case 1:
 #pragma unroll
-            for (int s = 2 * part; s < 2 * part + 2; s++)
-                R.x[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, xoff[s], sx, 0));
-            break;
-        case 2:
-        case 3:
-        case 4:
-        case 5:
-            R.w[part - 2] =
-                __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, woff + 16 * (part - 2), sw, 0));
-            break;
-        case 6:
-            R.w16 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, woff + 64, sw, 0);
-            R.dx[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, doff, sd, 0));
-            break;
-        default:
-            R.dx[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, doff + 8, sd, 0));
-            break;
-        }
-    };
+    for (int s = 0; s < 2; s++) {
+        const int q = tid + 256 * s;
+        doff[s] = (uint32_t)(((q >> 3) * nb + (q & 7)) * 8);
+    }
     auto load_stage = [&](MmqRegs &R, int kc) {
+        const int sx = kc * kMmqKB, sw = kc * (kMmqBlocks * kQ80Bytes), sd = kc * kMmqBlocks * 8;
 #pragma unroll
-        for (int part = 0; part < kMmqBlocks; part++) load_part(R, kc, part);
+        for (int s = 0; s < 4; s++)
+            R.x[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, xoff[s], sx, 0));
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+            R.w[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, woff + 16 * s, sw, 0));
+        R.w16 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, woff + 64, sw, 0);
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+            R.dx[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, doff[s], sd, 0));
     };
     auto store_stage = [&](MmqStage &S, const MmqRegs &R) {
 #pragma unroll
@@ -182,8 +163,11 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
         *reinterpret_cast<u32x4 *>(wr + 48) = qb1;
         S.dw[b0][wrow] = half_bits_to_float(d[0]);
         S.dw[b0 + 1][wrow] = half_bits_to_float(d[8] >> 16);
-        S.dx[2 * (tid & 3)][tid >> 2] = R.dx[0];
-        S.dx[2 * (tid & 3) + 1][tid >> 2] = R.dx[1];
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            int q = tid + 256 * s;
+            S.dx[q & 7][q >> 3] = R.dx[s];
+        }
     };
 
     v16f acc;
@@ -203,7 +187,7 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
     // in the same register layout as the int32 block sums.  That leaves two
     // VALU ops per output and block: convert S, then fma into the
     // accumulator.  The outer products of a pair are issued one pair ahead.
-    auto compute_stage = [&](const MmqStage &S, MmqRegs &R, int kc_load, auto with_loads) {
+    auto compute_stage = [&](const MmqStage &S) {
         v4i A[3], B[3];
         const uint8_t *xa = S.x + arow * kMmqRowStride + 16 * khalf;
         const uint8_t *wb = S.w + brow * kMmqRowStride + 16 * khalf;
@@ -227,7 +211,6 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
         v16i Sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[0], B[0], z, 0, 0, 0);
 #pragma unroll
         for (int b = 0; b < kMmqBlocks; b++) {
-            if constexpr (decltype(with_loads)::value) load_part(R, kc_load, b);
             if (b + 2 < kMmqBlocks) rd(b + 2, (b + 2) % 3);
             const v16i Sc = Sn;
             if (b + 1 < kMmqBlocks) Sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[(b + 1) % 3], B[(b + 1) % 3], z, 0, 0, 0);
@@ -253,29 +236,29 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
         }
     };
 
-    // Stages go in pairs through the two LDS buffers.  Inside the loop every
-    // load and LDS store is unconditional (past the last stage the loads
-    // re-read it, an L2 hit): with a branch around them the compiler cannot
-    // count the loads in flight, and its waits would then also wait for the
-    // loads just issued.  An odd last stage is computed after the loop.
+    // The loads are unconditional (past the last stage they re-read it, an L2
+    // hit): with a branch around them the compiler cannot count the loads in
+    // flight, and its wait before writing the older register buffer to LDS
+    // would then also wait for the loads just issued.
     MmqRegs R0, R1;
     const int last = nstage - 1;
     load_stage(R0, 0);
     load_stage(R1, min(1, last));
     store_stage(st[0], R0);
     __syncthreads();
-    int kc = 0;
-    for (; kc + 1 < nstage; kc += 2) {
-        // st[0] holds stage kc, R1 stage kc+1 (in flight); the loads of stage
-        // kc+2 into R0 are spread over this stage's blocks
-        compute_stage(st[0], R0, min(kc + 2, last), std::true_type{});
-        store_stage(st[1], R1);
+    for (int kc = 0; kc < nstage; kc += 2) {
+        // st[0] holds stage kc; R1 holds stage kc+1 (in flight)
+        load_stage(R0, min(kc + 2, last));
+        compute_stage(st[0]);
+        if (kc + 1 < nstage) store_stage(st[1], R1);
         __syncthreads();
-        compute_stage(st[1], R1, min(kc + 3, last), std::true_type{});
-        store_stage(st[0], R0);
-        __syncthreads();
+        if (kc + 1 < nstage) {
+            load_stage(R1, min(kc + 3, last));
+            compute_stage(st[1]);
+            if (kc + 2 < nstage) store_stage(st[0], R0);
+            __syncthreads();
+        }
     }
-    if (kc < nstage) compute_stage(st[0], R0, 0, std::false_type{});
 
     // Output element (row 8*(v/4) + 4*khalf + v%4, column lane%32) of the wave tile.
     const int col = n0 + wn * 32 + (lane & 31);
