@@ -55,6 +55,11 @@ def _load():
         lib.oracle_e4m3_matmul.argtypes = [P, P, P, I, I, I, P, P]
         lib.oracle_e4m3_matmul_sampled.argtypes = [P, P, P, I, I, P, P, P, P]
         lib.oracle_e4m3_gemv.argtypes = [P, P, ctypes.c_float, I, I, I, P, P]
+        lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+        lib.oracle_f32_to_f16_array.argtypes = [P, P, I]
+        lib.oracle_q8_0_dequant_f16.argtypes = [P, I, P, I, I]
+        lib.oracle_f16_gemm.argtypes = [P, P, I, I, I, P, P]
         lib.oracle_e4m3_gemv_sampled.argtypes = [P, P, ctypes.c_float, I, I, P, P, P, P]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -195,4 +200,33 @@ def e4m3_gemv_sampled(w, x, w_scale, tok, row):
     T = np.empty(len(tok), dtype=np.float64)
     _load().oracle_e4m3_gemv_sampled(_p(w), _p(x), ctypes.c_float(w_scale), w.shape[1], len(tok),
                                      _p(tok), _p(row), _p(y), _p(T))
+    return y, T
+
+
+def f32_to_f16(x) -> np.ndarray:
+    """IEEE round-to-nearest-even f32 -> fp16 bit patterns (uint16), same shape."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_f32_to_f16_array(_p(x), _p(out), x.size)
+    return out
+
+
+def q8_0_dequant_f16(w: np.ndarray, k: int) -> np.ndarray:
+    """Q8_0 rows [n, row_bytes] -> fp16 bit patterns [n, k]: fp16(d * q)."""
+    w = _c(w, np.uint8)
+    n = w.shape[0]
+    out = np.empty((n, k), dtype=np.uint16)
+    _load().oracle_q8_0_dequant_f16(_p(w), w.shape[1], _p(out), k, n)
+    return out
+
+
+def f16_gemm(w16: np.ndarray, x16: np.ndarray):
+    """fp16 bit patterns w16 [n, k], x16 [m, k] -> (y = x16 @ w16^T in fp64, sum|terms|)."""
+    w16 = _c(w16, np.uint16)
+    x16 = _c(x16, np.uint16)
+    n, k = w16.shape
+    m = x16.shape[0]
+    y = np.empty((m, n), dtype=np.float64)
+    T = np.empty((m, n), dtype=np.float64)
+    _load().oracle_f16_gemm(_p(w16), _p(x16), m, k, n, _p(y), _p(T))
     return y, T

@@ -343,3 +343,90 @@ void oracle_e4m3_gemv_sampled(const uint8_t *w, const float *x, float w_scale, i
     for (int64_t p = 0; p < npairs; p++)
         e4m3_gemv_dot(w + row[p] * k, x + tok[p] * k, k, (double)w_scale, &y[p], &tabs[p]);
 }
+
+/*
+ * fp16 mirror of the Q8_0 weights and the fp16 prefill GEMM ("f16_ffi.rs"
+ * page, memra-engine 0.81.0, module doc and the memra_q8_0_dequant_f16 /
+ * memra_f16_cvt / memra_f16_pp_gemm_pre declarations): the int8 quants are
+ * exact in fp16, rounding enters only at the d*q product's cast to fp16 and at
+ * the activation's f32 -> fp16 cast; the GEMM accumulates in f32 and writes
+ * f32.  Both casts are read as IEEE round-to-nearest-even with overflow to
+ * infinity and subnormals kept (the pages do not say; the plainest reading of
+ * a cast).
+ */
+uint16_t oracle_f32_to_f16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t exp = (u >> 23) & 0xFFu, man = u & 0x7FFFFFu;
+    if (exp == 0xFFu) return (uint16_t)(sign | 0x7C00u | (man ? 0x200u : 0u));   /* inf, NaN */
+    /* value = 1.man * 2^(exp-127) for normal f32 (f32 subnormals are far below fp16's range) */
+    int e = (int)exp - 127;
+    if (exp == 0) return sign;                         /* f32 zero or subnormal: rounds to zero */
+    uint32_t sig = man | 0x800000u;                    /* 24-bit significand, value = sig * 2^(e-23) */
+    /* target: integer multiple of the fp16 quantum at this exponent */
+    int q = e >= -14 ? e - 10 : -24;                   /* quantum exponent: 2^q (normal: 11 bits; subnormal: 2^-24) */
+    int shift = q - (e - 23);                          /* bits of sig below the quantum */
+    uint32_t mant;
+    if (shift >= 32) {
+        mant = 0;
+    } else if (shift <= 0) {
+        mant = sig << (-shift);
+    } else {
+        uint32_t keep = sig >> shift, rem = sig & ((1u << shift) - 1u), half = 1u << (shift - 1);
+        mant = keep + ((rem > half || (rem == half && (keep & 1u))) ? 1u : 0u);
+    }
+    /* mant * 2^q; renormalize */
+    if (mant == 0) return sign;
+    int E;
+    if (q == -24) {
+        if (mant < 1024u) return (uint16_t)(sign | mant);            /* subnormal */
+        E = -14;                                                      /* rounded up into the normals */
+        mant >>= 0;
+        if (mant >= 2048u) { mant >>= 1; E += 1; }
+    } else {
+        E = e;
+        if (mant >= 2048u) { mant >>= 1; E += 1; }                    /* carry out of the significand */
+    }
+    if (E > 15) return (uint16_t)(sign | 0x7C00u);                    /* overflow to infinity */
+    return (uint16_t)(sign | ((uint32_t)(E + 15) << 10) | (mant & 0x3FFu));
+}
+
+void oracle_f32_to_f16_array(const float *x, uint16_t *out, int64_t count) {
+    for (int64_t i = 0; i < count; i++) out[i] = oracle_f32_to_f16(x[i]);
+}
+
+/* Q8_0 rows -> row-major fp16: w16[r][32b+i] = fp16(d * q), d*q exact in f32. */
+void oracle_q8_0_dequant_f16(const uint8_t *w, int64_t row_bytes, uint16_t *w16, int64_t k, int64_t n) {
+    const int64_t nb = k / 32;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *blk = w + r * row_bytes + b * 34;
+            const float d = q8_0_scale(blk);
+            for (int i = 0; i < 32; i++) {
+                const float v = d * (float)(int8_t)blk[2 + i];
+                w16[r * k + b * 32 + i] = oracle_f32_to_f16(v);
+            }
+        }
+}
+
+static double f16_value(uint16_t h) { return (double)oracle_fp16_to_f32(h); }
+
+static void f16_dot(const uint16_t *wrow, const uint16_t *xrow, int64_t k, double *y, double *tabs) {
+    double acc = 0.0, aabs = 0.0;
+    for (int64_t i = 0; i < k; i++) {
+        double p = f16_value(xrow[i]) * f16_value(wrow[i]);
+        acc += p;
+        aabs += fabs(p);
+    }
+    *y = acc;
+    *tabs = aabs;
+}
+
+/* y[t][r] = sum_k x16[t][k] * w16[r][k] in fp64 (products of two fp16 are exact). */
+void oracle_f16_gemm(const uint16_t *w16, const uint16_t *x16, int64_t m, int64_t k, int64_t n, double *y,
+                     double *tabs) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t t = 0; t < m; t++) f16_dot(w16 + r * k, x16 + t * k, k, &y[t * n + r], &tabs[t * n + r]);
+}

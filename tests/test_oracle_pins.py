@@ -438,3 +438,66 @@ def test_e4m3_gemv_tiny_brute_force_in_exact_rationals():
         for r in range(n):
             exact = Fraction(float(ws)) * sum(Fraction(float(x[t, i])) * Fraction(float(dec[r, i])) for i in range(k))
             assert abs(Fraction(y[t, r]) - exact) <= abs(exact) * Fraction(1, 2**50) + Fraction(1, 2**1000)
+
+
+# --------------------------------------------------------------------------- fp16 mirror
+
+
+def _np_f16_bits(x):
+    with np.errstate(over="ignore"):
+        return np.asarray(x, np.float32).astype(np.float16).view(np.uint16)
+
+
+def test_f32_to_f16_matches_numpy_on_every_code_midpoint_and_neighbour():
+    # every finite fp16 value, the midpoints between neighbours (ties go to the
+    # even code), one f32 ulp either side of each midpoint, the overflow edge
+    codes = np.arange(0, 0x7C00, dtype=np.uint16)
+    vals = codes.view(np.float16).astype(np.float32)
+    mids = ((vals[:-1].astype(np.float64) + vals[1:].astype(np.float64)) / 2).astype(np.float32)
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    edge = np.array([65504, 65519.996, 65520, 65536, 1e30, np.inf, 2.0**-25, 2.0**-24, 1e-30], np.float32)
+    x = np.concatenate([vals, mids, up, dn, edge])
+    x = np.concatenate([x, -x])
+    assert np.array_equal(oracle.f32_to_f16(x), _np_f16_bits(x))
+
+
+def test_f32_to_f16_random_and_nan():
+    rng = np.random.default_rng(40)
+    x = (rng.standard_normal(200000) * 10.0 ** rng.uniform(-9, 6, 200000)).astype(np.float32)
+    assert np.array_equal(oracle.f32_to_f16(x), _np_f16_bits(x))
+    h = oracle.f32_to_f16(np.array([np.nan], np.float32))[0]
+    assert (h & 0x7C00) == 0x7C00 and (h & 0x3FF) != 0
+
+
+def test_q8_0_dequant_f16_closed_form_and_numpy():
+    # d = 1 (0x3C00): fp16(q) is exactly q
+    k = 64
+    w = workloads.pack_q8_0(np.tile(np.arange(-32, 32, dtype=np.int8), (2, 1)),
+                            np.full((2, 2), 1.0, np.float16))
+    assert np.array_equal(oracle.q8_0_dequant_f16(w, k).view(np.float16).astype(np.float32),
+                          np.tile(np.arange(-32, 32, dtype=np.float32), (2, 1)))
+    rng = np.random.default_rng(41)
+    n, k = 7, 512
+    w = workloads.q8_0_weights(n, k, rng)
+    q, d = workloads.unpack_q8_0(w, k)
+    ref = _np_f16_bits(d.astype(np.float32).repeat(32, axis=1) * q.astype(np.float32))
+    assert np.array_equal(oracle.q8_0_dequant_f16(w, k), ref)
+
+
+def test_f16_gemm_matches_fp64_matmul_and_one_hot():
+    rng = np.random.default_rng(42)
+    n, k, m = 33, 1024, 5
+    w16 = oracle.q8_0_dequant_f16(workloads.q8_0_weights(n, k, rng), k)
+    x16 = oracle.f32_to_f16(workloads.activations(m, k, rng, outliers=True))
+    y, T = oracle.f16_gemm(w16, x16)
+    W = w16.view(np.float16).astype(np.float64)
+    X = x16.view(np.float16).astype(np.float64)
+    assert np.all(np.abs(y - X @ W.T) <= 1e-12 * (np.abs(X) @ np.abs(W).T))
+    assert np.allclose(T, np.abs(X) @ np.abs(W).T, rtol=1e-12, atol=0)
+    oh = np.zeros((2, k), np.float32)
+    oh[0, 3] = 1.0
+    oh[1, 1000] = -2.0
+    y1, _ = oracle.f16_gemm(w16, oracle.f32_to_f16(oh))
+    assert np.array_equal(y1[0], W[:, 3])
+    assert np.array_equal(y1[1], -2.0 * W[:, 1000])
