@@ -12,7 +12,9 @@ The same JSON line also carries the prefill rows, each timed the same way:
 the m=512 MMQ GEMM (q8_1 quantize + int8 GEMM) at N in {4096, 5152, 20480}
 and the FP8-E4M3 GEMM (amax quantize + fp8 GEMM) at N=20480, with int8/fp8
 TOPS and their fraction of the matrix-core peak; the e4m3 decode GEMV
-(raw e4m3 weights, f32 activations) at m=1 and 9 on the head shape; a roofline object for the
+(raw e4m3 weights, f32 activations) at m=1 and 9 on the head shape; the fp16
+mirror prefill (f32 -> fp16 cast + fp16 GEMM, m=512, K=4096, N=20480, with the
+one-off Q8_0 -> fp16 dequant timed beside it); a roofline object for the
 dominant kernel (the GEMV), measured with HIP events on the launch stream;
 and the CPU oracle timed on the host cores on a bounded sample.
 
@@ -36,6 +38,7 @@ METRIC = "Q8_0 GEMV GB/s (m=1) + MMQ int8 TOPS (m=512), % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA
 FP8_PEAK_TFLOPS = 5000.0         # dense fp8 MFMA
+FP16_PEAK_TFLOPS = 2500.0        # dense fp16 MFMA
 ROTATE = 3
 
 
@@ -105,7 +108,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3", "e4m3_gemv", "copy"], default=None,
+    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3", "e4m3_gemv", "f16", "copy"], default=None,
                     help="run one part only (for profiler passes); 'copy' runs a plain 1 GiB device copy "
                          "that calibrates the HBM byte counters")
     args = ap.parse_args()
@@ -249,6 +252,37 @@ def main():
                            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         out["e4m3_gemv"] = e8
         del ws, w0
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- fp16 mirror prefill
+    if args.only in (None, "f16"):
+        m, k, n = 512, 4096, 20480
+        log("[bench] f16 mirror n=20480")
+        wq = torch.from_numpy(workloads.q8_0_weights(n, k, rng)).to(dev)
+        w16s = [torch.empty((n, k), dtype=torch.float16, device=dev) for _ in range(ROTATE)]
+        for w16 in w16s:
+            bqm.bqm_q8_0_dequant_f16(wq, k, w16)
+        x = torch.from_numpy(workloads.activations(m, k, rng, outliers=True)).to(dev)
+        x16 = torch.empty((m, k), dtype=torch.float16, device=dev)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        fns = [("cvt", lambda s: bqm.bqm_f16_cvt(x, x16)),
+               ("gemm", lambda s: bqm.bqm_f16_gemm(w16s[s % ROTATE], x16, y))]
+        timed_loop(torch, stream, args.warmup, fns)
+        total_ms, per = timed_loop(torch, stream, args.steps, fns)
+        dq = [("dequant", lambda s: bqm.bqm_q8_0_dequant_f16(wq, k, w16s[s % ROTATE]))]
+        timed_loop(torch, stream, 2, dq)
+        _, per_dq = timed_loop(torch, stream, args.steps, dq)
+        ops = 2.0 * m * n * k
+        tf = ops / (per["gemm"] * 1e-3) / 1e12
+        dq_bytes = q8_0_bytes(0, k, n) + 2 * n * k
+        out["f16_mirror_m512"] = {
+            "workload": "fp16 mirror prefill m=512, K=4096, N=20480: f32->fp16 cast + fp16 GEMM (f32 accumulate)",
+            "gemm_us": round(per["gemm"] * 1e3, 2), "cvt_us": round(per["cvt"] * 1e3, 2),
+            "tflops": round(tf, 1), "frac_fp16_peak": round(tf / FP16_PEAK_TFLOPS, 4),
+            "step_tflops": round(ops / (total_ms / args.steps * 1e-3) / 1e12, 1),
+            "dequant_us": round(per_dq["dequant"] * 1e3, 2),
+            "dequant_gbs": round(dq_bytes / (per_dq["dequant"] * 1e-3) / 1e9, 1)}
+        del w16s, wq, y
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU oracle baseline

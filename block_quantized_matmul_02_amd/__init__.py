@@ -45,8 +45,11 @@ def lib() -> ctypes.CDLL:
         L.bqm_e4m3_quantize_amax.argtypes = [P, P, P, F, I, I, P]
         L.bqm_e4m3_gemm.argtypes = [P, P, P, P, I, I, I, P]
         L.bqm_e4m3_gemv.argtypes = [P, P, F, P, I, I, I, P]
+        L.bqm_q8_0_dequant_f16.argtypes = [P, I64, P, I, I, P]
+        L.bqm_f16_cvt.argtypes = [P, P, I64, P]
+        L.bqm_f16_gemm.argtypes = [P, P, P, I, I, I, P]
         for fn in ("bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax",
-                   "bqm_e4m3_gemm", "bqm_e4m3_gemv"):
+                   "bqm_e4m3_gemm", "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm"):
             getattr(L, fn).restype = ctypes.c_int
         L.bqm_strerror.argtypes = [I]
         L.bqm_strerror.restype = ctypes.c_char_p
@@ -183,4 +186,44 @@ def bqm_e4m3_gemv(w, x, w_scale: float, y=None):
     _check(y, torch.float32, "y", (m, n))
     rc = lib().bqm_e4m3_gemv(_ptr(w), _ptr(x), ctypes.c_float(w_scale), _ptr(y), m, k, n, _stream(w))
     _raise("bqm_e4m3_gemv", rc)
+    return y
+
+
+def bqm_q8_0_dequant_f16(w, k: int, w16=None):
+    """fp16 mirror of Q8_0 rows ``w [n, row_bytes]`` -> ``w16 [n, k]`` (torch.float16) = fp16(d * q)."""
+    import torch
+
+    n = w.shape[0]
+    _check(w, torch.uint8, "w")
+    if w16 is None:
+        w16 = torch.empty((n, k), dtype=torch.float16, device=w.device)
+    _check(w16, torch.float16, "w16", (n, k))
+    _raise("bqm_q8_0_dequant_f16", lib().bqm_q8_0_dequant_f16(_ptr(w), w.shape[1], _ptr(w16), k, n, _stream(w)))
+    return w16
+
+
+def bqm_f16_cvt(x, x16=None):
+    """f32 -> fp16 cast (round to nearest even) of a contiguous tensor, same shape."""
+    import torch
+
+    _check(x, torch.float32, "x")
+    if x16 is None:
+        x16 = torch.empty(x.shape, dtype=torch.float16, device=x.device)
+    _check(x16, torch.float16, "x16", tuple(x.shape))
+    _raise("bqm_f16_cvt", lib().bqm_f16_cvt(_ptr(x), _ptr(x16), x.numel(), _stream(x)))
+    return x16
+
+
+def bqm_f16_gemm(w16, x16, y=None):
+    """fp16 GEMM: ``w16 [n, k]`` and ``x16 [m, k]`` (torch.float16) -> f32 ``y [m, n]`` = x16 @ w16^T."""
+    import torch
+
+    n, k = w16.shape
+    m = x16.shape[0]
+    _check(w16, torch.float16, "w16")
+    _check(x16, torch.float16, "x16", (m, k))
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x16.device)
+    _check(y, torch.float32, "y", (m, n))
+    _raise("bqm_f16_gemm", lib().bqm_f16_gemm(_ptr(w16), _ptr(x16), _ptr(y), m, k, n, _stream(w16)))
     return y

@@ -159,6 +159,39 @@ int bqm_e4m3_gemm(const uint8_t *w, const uint8_t *xq, const float *scales, floa
 int bqm_e4m3_gemv(const uint8_t *w, const float *x, float w_scale, float *y, int m, int k, int n,
                   void *stream);
 
+/*
+ * fp16 mirror prefill path ("f16_ffi.rs" page, module doc and the
+ * memra_q8_0_dequant_f16 / memra_f16_cvt / memra_f16_pp_gemm_pre
+ * declarations): a resident fp16 copy of a Q8_0 projection, made once, an
+ * f32 -> fp16 activation cast, and an fp16 GEMM with f32 accumulation and
+ * f32 output.  Rounding enters only at the two casts (IEEE round to nearest
+ * even, overflow to infinity, subnormals kept).
+ *
+ * bqm_q8_0_dequant_f16: w16[r][32b+i] = fp16(d * q) of block b of row r.
+ *   w          : Q8_0 rows [n][w_row_bytes], 4-byte aligned, w_row_bytes % 4
+ *                == 0 and >= k/32*34.
+ *   w16        : fp16 [n][k] out (row-major), 16-byte aligned.
+ *   k >= 64, n >= 1 (else BQM_EINVAL); k % 64 == 0 (else BQM_EUNSUPPORTED).
+ */
+int bqm_q8_0_dequant_f16(const uint8_t *w, int64_t w_row_bytes, uint16_t *w16, int k, int n,
+                         void *stream);
+
+/*
+ * bqm_f16_cvt: x16[i] = fp16(x[i]) for count values.
+ *   x : f32 [count], 16-byte aligned;  x16 : fp16 [count] out, 8-byte aligned.
+ *   count >= 1 (else BQM_EINVAL).
+ */
+int bqm_f16_cvt(const float *x, uint16_t *x16, int64_t count, void *stream);
+
+/*
+ * bqm_f16_gemm: y[t][r] = sum_k x16[t][k] * w16[r][k], f32 accumulation.
+ *   w16 : fp16 [n][k], 16-byte aligned;  x16 : fp16 [m][k], 16-byte aligned;
+ *   y   : f32 [m][n] out, 4-byte aligned, fully overwritten.
+ *   m, n >= 1, k >= 64 (else BQM_EINVAL); k % 64 == 0 (else BQM_EUNSUPPORTED).
+ */
+int bqm_f16_gemm(const uint16_t *w16, const uint16_t *x16, float *y, int m, int k, int n,
+                 void *stream);
+
 /* Text for a return code; never NULL, static storage. */
 const char *bqm_strerror(int rc);
 

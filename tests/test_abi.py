@@ -32,7 +32,7 @@ def declared_symbols():
 def test_header_declares_the_calls_and_strerror():
     assert declared_symbols() == sorted([
         "bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax", "bqm_e4m3_gemm",
-        "bqm_e4m3_gemv", "bqm_strerror"])
+        "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm", "bqm_strerror"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -132,6 +132,33 @@ def test_e4m3_gemv_validation(L):
     assert f(MIS2, B16, F(1.0), D16, 1, 4096, 8, NUL) == 2
     assert f(A16, P(0x200004), F(1.0), D16, 1, 4096, 8, NUL) == 2      # x 16-byte alignment
     assert f(A16, B16, F(1.0), P(0x400002), 1, 4096, 8, NUL) == 2
+
+
+def test_f16_mirror_validation(L):
+    d = L.bqm_q8_0_dequant_f16
+    rb = 4096 // 32 * 34
+    assert d(NUL, rb, B16, 4096, 8, NUL) == 1
+    assert d(A16, rb, NUL, 4096, 8, NUL) == 1
+    assert d(A16, rb, B16, 32, 8, NUL) == 1                 # k < 64
+    assert d(A16, rb, B16, 4096, 0, NUL) == 1
+    assert d(A16, rb, B16, 4096 + 32, 8, NUL) == 2          # k % 64
+    assert d(A16, rb - 4, B16, 4096, 8, NUL) == 2           # row shorter than k/32*34
+    assert d(A16, rb + 2, B16, 4096, 8, NUL) == 2           # row bytes % 4
+    assert d(MIS2, rb, B16, 4096, 8, NUL) == 2
+    assert d(A16, rb, P(0x200008), 4096, 8, NUL) == 2       # w16 16-byte alignment
+    c = L.bqm_f16_cvt
+    assert c(NUL, B16, 8, NUL) == 1
+    assert c(A16, NUL, 8, NUL) == 1
+    assert c(A16, B16, 0, NUL) == 1
+    assert c(P(0x100004), B16, 8, NUL) == 2
+    assert c(A16, P(0x200004), 8, NUL) == 2
+    g = L.bqm_f16_gemm
+    assert g(NUL, B16, C16, 1, 64, 8, NUL) == 1
+    assert g(A16, B16, C16, 0, 64, 8, NUL) == 1
+    assert g(A16, B16, C16, 1, 32, 8, NUL) == 1
+    assert g(A16, B16, C16, 1, 96, 8, NUL) == 2             # k % 64
+    assert g(A16, MIS2, C16, 1, 64, 8, NUL) == 2
+    assert g(A16, B16, P(0x300002), 1, 64, 8, NUL) == 2
 
 
 def test_product_path_never_touches_the_oracle():
