@@ -170,7 +170,7 @@ def main():
             "ms_per_step": round(ms_step, 5),
             "config": {"workload": "decode head GEMV: m=1, K=4096, N=64448, Q8_0 weights, q8_1 activations",
                        "m": m, "k": k, "n": n, "weight_copies_rotated": ROTATE, "parallelism": "none"},
-            "roofline": {"bound": "hbm", "kernel": "q8_0_gemv_kernel<1, false>", "achieved": round(achieved, 1),
+            "roofline": {"bound": "hbm", "kernel": "q8_0_gemv_kernel<1, false, 1>", "achieved": round(achieved, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": recorded_traffic(), "bytes_per_launch": gemv_bytes,
                          "avg_launch_us": round(per["gemv"] * 1e3, 3)},
