@@ -61,6 +61,7 @@ def _load():
         lib.oracle_q8_0_dequant_f16.argtypes = [P, I, P, I, I]
         lib.oracle_f16_gemm.argtypes = [P, P, I, I, I, P, P]
         lib.oracle_e4m3_gemv_sampled.argtypes = [P, P, ctypes.c_float, I, I, P, P, P, P]
+        lib.oracle_q8_0_matmul_e4m3.argtypes = [P, I, P, P, I, I, I, P, P]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -229,4 +230,18 @@ def f16_gemm(w16: np.ndarray, x16: np.ndarray):
     y = np.empty((m, n), dtype=np.float64)
     T = np.empty((m, n), dtype=np.float64)
     _load().oracle_f16_gemm(_p(w16), _p(x16), m, k, n, _p(y), _p(T))
+    return y, T
+
+
+def q8_0_matmul_e4m3(w: np.ndarray, xq: np.ndarray, xds: np.ndarray, k: int):
+    """The accumulator instrument's f32 arm: the Q8_0 x q8_1 matmul with every
+    quant byte read as an e4m3 code.  Returns (y [m, n] fp64, sum|terms| [m, n])."""
+    w = _c(w, np.uint8)
+    xq = _c(xq, np.int8).view(np.uint8)
+    xds = _c(xds, np.float32)
+    n = w.shape[0]
+    m = xq.shape[0]
+    y = np.empty((m, n), dtype=np.float64)
+    T = np.empty((m, n), dtype=np.float64)
+    _load().oracle_q8_0_matmul_e4m3(_p(w), w.shape[1], _p(xq), _p(xds), m, k, n, _p(y), _p(T))
     return y, T

@@ -430,3 +430,44 @@ void oracle_f16_gemm(const uint16_t *w16, const uint16_t *x16, int64_t m, int64_
     for (int64_t r = 0; r < n; r++)
         for (int64_t t = 0; t < m; t++) f16_dot(w16 + r * k, x16 + t * k, k, &y[t * n + r], &tabs[t * n + r]);
 }
+
+/*
+ * The accumulator instrument's f32 arm ("accprobe_bench.rs" page, memra-engine
+ * 0.124.1, module doc): the Q8_0 MMQ with the int8 MMA swapped for an e4m3 x
+ * e4m3 MMA that accumulates in f32, on the same bytes, with the same fold by
+ * the two block scales every 32 values.  Every quant byte, weight and
+ * activation, is read as an OCP E4M3FN code instead of an int8:
+ *   y[t][n] = sum_b d_w[n][b] * d_x[t][b] * sum_i dec(q_w[n][b][i]) * dec(q_x[t][b][i])
+ * in fp64 (the block sum of e4m3 products is exact; each block term carries
+ * one fp64 rounding).  tabs = sum_b |d_w d_x| * sum_i |dec * dec|, the sum of
+ * the magnitudes of every product term.  The instrument's bytes avoid the NaN
+ * codes (magnitudes <= 126, module doc), so every term is finite.
+ */
+static void q8_0_e4m3_dot(const uint8_t *wrow, const uint8_t *xrow, const float *xdsrow, int64_t nb,
+                          double *y, double *tabs) {
+    double acc = 0.0, aabs = 0.0;
+    for (int64_t b = 0; b < nb; b++) {
+        const uint8_t *blk = wrow + b * Q8_0_BYTES;
+        double s = 0.0, sabs = 0.0;
+        for (int i = 0; i < QK; i++) {
+            double p = e4m3_table[blk[2 + i]] * e4m3_table[xrow[b * QK + i]];
+            s += p;
+            sabs += fabs(p);
+        }
+        double scale = (double)q8_0_scale(blk) * (double)xdsrow[2 * b];
+        acc += scale * s;
+        aabs += fabs(scale) * sabs;
+    }
+    *y = acc;
+    *tabs = aabs;
+}
+
+void oracle_q8_0_matmul_e4m3(const uint8_t *w, int64_t row_bytes, const uint8_t *xq, const float *xds,
+                             int64_t m, int64_t k, int64_t n, double *y, double *tabs) {
+    int64_t nb = k / QK;
+    e4m3_fill_table();
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t t = 0; t < m; t++)
+            q8_0_e4m3_dot(w + r * row_bytes, xq + t * k, xds + t * nb * 2, nb, &y[t * n + r], &tabs[t * n + r]);
+}

@@ -501,3 +501,71 @@ def test_f16_gemm_matches_fp64_matmul_and_one_hot():
     y1, _ = oracle.f16_gemm(w16, oracle.f32_to_f16(oh))
     assert np.array_equal(y1[0], W[:, 3])
     assert np.array_equal(y1[1], -2.0 * W[:, 1000])
+
+
+# --------------------------------------------------------------------------- accumulator instrument, f32 arm
+
+
+def _torch_e4m3(b):
+    return torch.from_numpy(np.ascontiguousarray(b).view(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+@pytest.mark.parametrize("dist", ["wide", "mid"])
+def test_q8_0_matmul_e4m3_matches_torch_decoded_fp64_matmul(dist):
+    # bytes decoded by torch's float8_e4m3fn, scales by numpy's float16, one
+    # fp64 einsum per block: an independent route to the same definition
+    rng = np.random.default_rng(7)
+    n, k, m = 29, 512, 6
+    w = workloads.accprobe_weights(n, k, rng, dist)
+    xq, xds = workloads.accprobe_activations(m, k, rng, dist)
+    y, T = oracle.q8_0_matmul_e4m3(w, xq, xds, k)
+    q, d = workloads.unpack_q8_0(w, k)
+    Wq = _torch_e4m3(q).reshape(n, k // 32, 32)
+    Xq = _torch_e4m3(xq).reshape(m, k // 32, 32)
+    blk = np.einsum("tbi,nbi->tnb", Xq, Wq)
+    scale = xds[:, None, :, 0].astype(np.float64) * d.astype(np.float64)[None, :, :]
+    ref = (scale * blk).sum(axis=2)
+    babs = np.einsum("tbi,nbi->tnb", np.abs(Xq), np.abs(Wq))
+    assert np.all(np.abs(y - ref) <= 1e-13 * T)
+    assert np.allclose(T, (np.abs(scale) * babs).sum(axis=2), rtol=1e-13, atol=0)
+    # the int8 reading of the same bytes is a different number
+    y8, _ = oracle.q8_0_matmul(w, xq, xds, k)
+    assert not np.allclose(y, y8)
+
+
+def test_q8_0_matmul_e4m3_one_hot_and_closed_form():
+    k, n = 256, 4
+    rng = np.random.default_rng(3)
+    w = workloads.accprobe_weights(n, k, rng)
+    q, d = workloads.unpack_q8_0(w, k)
+    # one activation byte 0x38 (e4m3 1.0) at column 77 with d_x = 1: y = d_w * dec(q_w) exactly
+    xq = np.zeros((1, k), np.int8)
+    xq[0, 77] = 0x38
+    xds = np.zeros((1, k // 32, 2), np.float32)
+    xds[0, :, 0] = 1.0
+    y, _ = oracle.q8_0_matmul_e4m3(w, xq, xds, k)
+    expect = d[:, 77 // 32].astype(np.float64) * _torch_e4m3(q[:, 77])
+    assert np.array_equal(y[0], expect)
+    # constant bytes and scales: y = K * dec(cw) * dec(cx) * d_w * d_x
+    cw, cx = np.int8(0x44), np.int8(-0x3B)              # 0x44 = 3.0, 0xC5 = -3.25 (OCP E4M3FN)
+    wc = workloads.pack_q8_0(np.full((2, k), cw, np.int8), np.full((2, k // 32), 0.015625, np.float16))
+    xqc = np.full((3, k), cx, np.int8)
+    xdsc = np.zeros((3, k // 32, 2), np.float32)
+    xdsc[:, :, 0] = 0.5
+    yc, Tc = oracle.q8_0_matmul_e4m3(wc, xqc, xdsc, k)
+    assert np.all(yc == k * 3.0 * -3.25 * 0.015625 * 0.5)
+    assert np.all(Tc == -yc)
+
+
+@pytest.mark.parametrize("dist", ["wide", "mid"])
+def test_accprobe_bytes_are_finite_in_both_readings(dist):
+    rng = np.random.default_rng(11)
+    w = workloads.accprobe_weights(64, 1024, rng, dist)
+    xq, _ = workloads.accprobe_activations(64, 1024, rng, dist)
+    q, _ = workloads.unpack_q8_0(w, 1024)
+    for b in (q, xq):
+        assert np.abs(b.astype(np.int16)).max() <= 126
+        assert not np.any((b.view(np.uint8) & 0x7F) == 0x7F)
+        assert np.all(np.isfinite(_torch_e4m3(b)))
+    if dist == "wide":
+        assert len(np.unique(q)) == 252

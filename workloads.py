@@ -26,6 +26,18 @@ Draw order per call (fixed; changing it changes every workload):
 ``e4m3_weights``: ``normal(0, 0.02, (N, K))``; the per-tensor scale is
 ``max|w| / 448`` and the codes are torch's ``float8_e4m3fn`` cast of
 ``w / scale`` (a library conversion, not this project's encoder).
+``accprobe_weights`` / ``accprobe_activations`` (the accumulator
+instrument's quantizer-free bytes, "accprobe_bench.rs" page (memra-engine
+0.124.1), fns ``synth_w_q8_0`` and ``synth_act_q8_1``: quant magnitudes at
+most 126, so every byte is finite and non-NaN read as int8 or as e4m3):
+quants first -- ``wide``: ``integers(-126, 126, (N, K))`` with every value
+``v >= -1`` moved up by one, i.e. uniform over -126..126 without -1 (int8 -1
+is byte 0xFF, which the page's own magnitude clamp lets through although it is
+an e4m3 NaN code); ``mid``: magnitude
+``0x30 + integers(0, 32)`` (e4m3 normals, mid exponents) with the sign bit
+``integers(0, 2)`` -- then scales, ``uniform(0.01, 0.03)`` rounded to fp16
+for weights and ``uniform(0.0125, 0.0273)`` f32 for activations (their sum
+slot is 0: the instrument's activation records carry no sum term).
 """
 from __future__ import annotations
 
@@ -87,6 +99,38 @@ def e4m3_weights(n: int, k: int, rng: np.random.Generator):
     v = np.clip(w / w_scale, -448.0, 448.0).astype(np.float32)
     codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
     return codes, float(w_scale)
+
+
+def _accprobe_quants(rows: int, k: int, rng: np.random.Generator, dist: str) -> np.ndarray:
+    if dist == "wide":
+        # -126..126 without -1: int8 -1 is byte 0xFF, an e4m3 NaN code
+        v = rng.integers(-126, 126, size=(rows, k), dtype=np.int16)
+        return np.where(v >= -1, v + 1, v).astype(np.int8)
+    if dist == "mid":
+        mag = (0x30 + rng.integers(0, 32, size=(rows, k))).astype(np.uint8)
+        sign = (rng.integers(0, 2, size=(rows, k)).astype(np.uint8) << 7).astype(np.uint8)
+        return (mag | sign).view(np.int8)
+    raise ValueError(f"unknown byte distribution {dist!r}")
+
+
+def accprobe_weights(n: int, k: int, rng: np.random.Generator, dist: str = "wide") -> np.ndarray:
+    """Q8_0 rows whose quant bytes are non-NaN as int8 and as e4m3; fp16 scales in [0.01, 0.03]."""
+    quants = _accprobe_quants(n, k, rng, dist)
+    scales = rng.uniform(0.01, 0.03, size=(n, k // QK)).astype(np.float16)
+    return pack_q8_0(quants, scales)
+
+
+def accprobe_activations(m: int, k: int, rng: np.random.Generator, dist: str = "wide"):
+    """Pre-quantized activations (xq int8 [m, K], xds f32 [m, K/32, 2]) with the same byte rule."""
+    xq = _accprobe_quants(m, k, rng, dist)
+    xds = np.zeros((m, k // QK, 2), dtype=np.float32)
+    xds[:, :, 0] = rng.uniform(0.0125, 0.0273, size=(m, k // QK)).astype(np.float32)
+    return xq, xds
+
+
+# The accumulator instrument's shape sheet (K -> N), "accprobe_bench.rs", fn main.
+ACCPROBE_SHAPES_27B = [(5120, 12288), (5120, 1024), (6144, 5120), (5120, 17408), (17408, 5120), (5120, 5120)]
+ACCPROBE_SHAPES_1P7B = [(2048, 2048), (2048, 1024), (2048, 2048), (2048, 6144), (6144, 2048)]
 
 
 # The workloads of the five measured configurations, by what they are.
