@@ -14,7 +14,10 @@ and the FP8-E4M3 GEMM (amax quantize + fp8 GEMM) at N=20480, with int8/fp8
 TOPS and their fraction of the matrix-core peak; the e4m3 decode GEMV
 (raw e4m3 weights, f32 activations) at m=1 and 9 on the head shape; the fp16
 mirror prefill (f32 -> fp16 cast + fp16 GEMM, m=512, K=4096, N=20480, with the
-one-off Q8_0 -> fp16 dequant timed beside it); a roofline object for the
+one-off Q8_0 -> fp16 dequant timed beside it); the accumulator instrument
+(the MMQ with its int8 MFMA + s32 block sums against the same kernel with
+fp8 MFMAs + f32 block sums, m=512, the 27B projection shapes, both arms timed
+interleaved per rep, medians, geomean of the ratio); a roofline object for the
 dominant kernel (the GEMV), measured with HIP events on the launch stream;
 and the CPU oracle timed on the host cores on a bounded sample.
 
@@ -108,7 +111,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3", "e4m3_gemv", "f16", "copy"], default=None,
+    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3", "e4m3_gemv", "f16", "accprobe", "copy"], default=None,
                     help="run one part only (for profiler passes); 'copy' runs a plain 1 GiB device copy "
                          "that calibrates the HBM byte counters")
     args = ap.parse_args()
@@ -284,6 +287,51 @@ def main():
             "dequant_gbs": round(dq_bytes / (per_dq["dequant"] * 1e-3) / 1e9, 1)}
         del w16s, wq, y
         torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- accumulator instrument
+    if args.only in (None, "accprobe"):
+        m, reps, batch = 512, 9, 10
+        probe = {}
+        for dist in ("wide", "mid"):
+            cells, ln_sum = {}, 0.0
+            for k, n in workloads.ACCPROBE_SHAPES_27B:
+                log(f"[bench] accprobe {dist} {k}->{n}")
+                w = torch.from_numpy(workloads.accprobe_weights(n, k, rng, dist)).to(dev)
+                xq_h, xds_h = workloads.accprobe_activations(m, k, rng, dist)
+                xq = torch.from_numpy(xq_h).to(dev)
+                xds = torch.from_numpy(xds_h).to(dev)
+                y = torch.empty((m, n), dtype=torch.float32, device=dev)
+                arms = {"f32": lambda: bqm.bqm_q8_0_gemm_f8acc(w, xq, xds, y),
+                        "s32": lambda: bqm.bqm_q8_0_gemm(w, xq, xds, y)}
+                for fn in arms.values():
+                    for _ in range(3):
+                        fn()
+                t = {"f32": [], "s32": []}
+                for _ in range(reps):
+                    for arm in ("f32", "s32"):           # interleaved inside each rep
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        for _ in range(batch):
+                            arms[arm]()
+                        e1.record(stream)
+                        e1.synchronize()
+                        t[arm].append(e0.elapsed_time(e1) / batch)
+                a, b = sorted(t["f32"])[reps // 2], sorted(t["s32"])[reps // 2]
+                ratio = a / b
+                flop = 2.0 * m * k * n
+                cells[f"{k}->{n}"] = {"f32acc_us": round(a * 1e3, 2), "s32acc_us": round(b * 1e3, 2),
+                                      "ratio": round(ratio, 4), "delta_pp": round(100 * (ratio - 1), 1),
+                                      "f32_tflop": round(flop / (a * 1e-3) / 1e12, 1),
+                                      "s32_tflop": round(flop / (b * 1e-3) / 1e12, 1)}
+                ln_sum += np.log(ratio)
+                del w, xq, xds, y
+            geo = float(np.exp(ln_sum / len(cells)))
+            probe[dist] = {"shapes": cells, "geomean_ratio": round(geo, 4), "delta_pp": round(100 * (geo - 1), 1)}
+        torch.cuda.empty_cache()
+        out["accprobe_m512"] = {"workload": "accumulator instrument, m=512, 27B projection shapes: the MMQ with "
+                                            "int8 MFMA + s32 block sums (s32) vs fp8 MFMA + f32 block sums (f32), "
+                                            "same tiles and fold count; medians of 9 interleaved reps of 10 launches",
+                                **probe}
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu and args.only in (None, "gemv"):

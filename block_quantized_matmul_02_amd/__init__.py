@@ -42,6 +42,7 @@ def lib() -> ctypes.CDLL:
         L.bqm_q8_1_quantize.argtypes = [P, P, P, I, I, P]
         L.bqm_q8_0_gemv.argtypes = [P, I64, P, P, P, I, I, I, P]
         L.bqm_q8_0_gemm.argtypes = [P, I64, P, P, P, I, I, I, P]
+        L.bqm_q8_0_gemm_f8acc.argtypes = [P, I64, P, P, P, I, I, I, P]
         L.bqm_e4m3_quantize_amax.argtypes = [P, P, P, F, I, I, P]
         L.bqm_e4m3_gemm.argtypes = [P, P, P, P, I, I, I, P]
         L.bqm_e4m3_gemv.argtypes = [P, P, F, P, I, I, I, P]
@@ -49,7 +50,7 @@ def lib() -> ctypes.CDLL:
         L.bqm_f16_cvt.argtypes = [P, P, I64, P]
         L.bqm_f16_gemm.argtypes = [P, P, P, I, I, I, P]
         for fn in ("bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax",
-                   "bqm_e4m3_gemm", "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm"):
+                   "bqm_e4m3_gemm", "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm", "bqm_q8_0_gemm_f8acc"):
             getattr(L, fn).restype = ctypes.c_int
         L.bqm_strerror.argtypes = [I]
         L.bqm_strerror.restype = ctypes.c_char_p
@@ -135,6 +136,17 @@ def bqm_q8_0_gemm(w, xq, xds, y=None):
     m, y = _q8_0_args(w, xq, xds, y, k, n)
     rc = lib().bqm_q8_0_gemm(_ptr(w), w.shape[1], _ptr(xq), _ptr(xds), _ptr(y), m, k, n, _stream(w))
     _raise("bqm_q8_0_gemm", rc)
+    return y
+
+
+def bqm_q8_0_gemm_f8acc(w, xq, xds, y=None):
+    """The accumulator instrument's f32 arm: bqm_q8_0_gemm with the quant bytes read as e4m3
+    and multiplied on the fp8 matrix cores (f32 accumulate); same arguments."""
+    n = w.shape[0]
+    k = xq.shape[1]
+    m, y = _q8_0_args(w, xq, xds, y, k, n)
+    rc = lib().bqm_q8_0_gemm_f8acc(_ptr(w), w.shape[1], _ptr(xq), _ptr(xds), _ptr(y), m, k, n, _stream(w))
+    _raise("bqm_q8_0_gemm_f8acc", rc)
     return y
 
 

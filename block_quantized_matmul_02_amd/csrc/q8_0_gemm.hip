@@ -33,6 +33,17 @@
 //    lane of a half-wave reads the same four rows).
 //  * Global loads are range-checked buffer loads: ragged m and n tails read
 //    zeros (zero scales), and only in-range outputs are stored.
+//
+// The same kernel with its accumulator as the one free variable is the
+// accumulator instrument ("accprobe_bench.rs" page, memra-engine 0.124.1,
+// module doc): the F8ACC arm reads every quant byte as an OCP e4m3 code and
+// replaces the int8 MFMA of a block by two v_mfma_f32_32x32x16_fp8_fp8 that
+// accumulate in f32 (the low and high 8 bytes of each lane's 16-byte operand,
+// the same k set for both operands).  Tiles, LDS, loads, launch and fold count
+// are unchanged; the fold skips the int32 -> f32 convert, since the block sum
+// already is f32.
+#include <type_traits>
+
 #include "bqmm_internal.h"
 
 namespace bqm {
@@ -68,6 +79,7 @@ struct MmqRegs {
     float dx[2];     // 2 (row, block) activation scales
 };
 
+template <bool F8ACC>
 __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *__restrict__ w, int64_t w_row_bytes,
                                                               const int8_t *__restrict__ xq,
                                                               const float *__restrict__ xds, float *__restrict__ y,
@@ -202,31 +214,52 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
             SA[p] = S.dx[2 * p + khalf][arow];
             SB[p] = S.dw[2 * p + khalf][brow];
         }
-        const v16i z = {0};
         const v32f z32 = {0};
         v32f P[2];
         rd(0, 0);
         rd(1, 1);
         P[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(SA[0], SB[0], z32, 0, 0, 0);
-        v16i Sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[0], B[0], z, 0, 0, 0);
+        // the block sums of one 32x32 tile: int32 from the int8 MFMA, or f32
+        // from two fp8 MFMAs over the same bytes
+        using BlockSum = typename std::conditional<F8ACC, v16f, v16i>::type;
+        auto block_sum = [&](const v4i &a, const v4i &b) -> BlockSum {
+            if constexpr (F8ACC) {
+                const v16f zf = {0};
+                const long alo = ((long)(uint32_t)a[1] << 32) | (uint32_t)a[0];
+                const long ahi = ((long)(uint32_t)a[3] << 32) | (uint32_t)a[2];
+                const long blo = ((long)(uint32_t)b[1] << 32) | (uint32_t)b[0];
+                const long bhi = ((long)(uint32_t)b[3] << 32) | (uint32_t)b[2];
+                const v16f lo = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(alo, blo, zf, 0, 0, 0);
+                return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(ahi, bhi, lo, 0, 0, 0);
+            } else {
+                const v16i z = {0};
+                return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
+            }
+        };
+        BlockSum Sn = block_sum(A[0], B[0]);
 #pragma unroll
         for (int b = 0; b < kMmqBlocks; b++) {
             if (b + 2 < kMmqBlocks) rd(b + 2, (b + 2) % 3);
-            const v16i Sc = Sn;
-            if (b + 1 < kMmqBlocks) Sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[(b + 1) % 3], B[(b + 1) % 3], z, 0, 0, 0);
+            const BlockSum Sc = Sn;
+            if (b + 1 < kMmqBlocks) Sn = block_sum(A[(b + 1) % 3], B[(b + 1) % 3]);
             if ((b & 1) == 0 && b + 2 < kMmqBlocks)
                 P[((b + 2) >> 1) & 1] =
                     __builtin_amdgcn_mfma_f32_32x32x1f32(SA[(b + 2) >> 1], SB[(b + 2) >> 1], z32, 0, 0, 0);
             // Issue those MFMAs before the fold below (they then run under the
             // fold's VALU work instead of stalling the next block's fold): the
             // empty asm claims to modify the accumulators, so no fold
-            // instruction can move above it, and it reads Sn, so the int8
+            // instruction can move above it, and it reads Sn, so the block-sum
             // MFMA cannot move below it.
             asm volatile("" : "+v"(Sn), "+v"(acc));
             const v32f &Pc = P[(b >> 1) & 1];
             const int h = 16 * (b & 1);
 #pragma unroll
-            for (int v = 0; v < 16; v++) acc[v] = __builtin_fmaf((float)Sc[v], Pc[h + v], acc[v]);
+            for (int v = 0; v < 16; v++) {
+                if constexpr (F8ACC)
+                    acc[v] = __builtin_fmaf(Sc[v], Pc[h + v], acc[v]);
+                else
+                    acc[v] = __builtin_fmaf((float)Sc[v], Pc[h + v], acc[v]);
+            }
             // Keep each block's group (reads for b+2, MFMAs for b+1, fold of
             // b) in this order: an empty asm that reads and writes the
             // accumulators stops the compiler from hoisting every block's loads
@@ -271,11 +304,10 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
     }
 }
 
-}  // namespace bqm
-
-extern "C" int bqm_q8_0_gemm(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y,
-                             int m, int k, int n, void *stream) {
-    using namespace bqm;
+// Checks shared by both arms, then the launch.
+template <bool F8ACC>
+static int launch_mmq(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y, int m,
+                      int k, int n, void *stream) {
     if (!w || !xq || !xds || !y) return BQM_EINVAL;
     if (m < 1 || k < 256 || n < 1) return BQM_EINVAL;
     if (k % 256 != 0) return BQM_EUNSUPPORTED;
@@ -286,7 +318,19 @@ extern "C" int bqm_q8_0_gemm(const uint8_t *w, int64_t w_row_bytes, const int8_t
     const int64_t tiles = (int64_t)((n + kMmqBN - 1) / kMmqBN) * ((m + kMmqBM - 1) / kMmqBM);
     if (tiles > 0x7FFFFFFF) return BQM_EUNSUPPORTED;
     dim3 grid((unsigned)tiles);
-    hipLaunchKernelGGL(q8_0_gemm_kernel, grid, dim3(kMmqThreads), 0, as_stream(stream), w, w_row_bytes, xq, xds, y, m,
-                       k, n);
+    hipLaunchKernelGGL(q8_0_gemm_kernel<F8ACC>, grid, dim3(kMmqThreads), 0, as_stream(stream), w, w_row_bytes, xq,
+                       xds, y, m, k, n);
     return launch_status();
+}
+
+}  // namespace bqm
+
+extern "C" int bqm_q8_0_gemm(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y,
+                             int m, int k, int n, void *stream) {
+    return bqm::launch_mmq<false>(w, w_row_bytes, xq, xds, y, m, k, n, stream);
+}
+
+extern "C" int bqm_q8_0_gemm_f8acc(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds,
+                                   float *y, int m, int k, int n, void *stream) {
+    return bqm::launch_mmq<true>(w, w_row_bytes, xq, xds, y, m, k, n, stream);
 }

@@ -103,6 +103,20 @@ int bqm_q8_0_gemm(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const
                   float *y, int m, int k, int n, void *stream);
 
 /*
+ * The accumulator instrument's f32 arm ("accprobe_bench.rs" page, module
+ * doc): bqm_q8_0_gemm with its accumulator as the one free variable.  Same
+ * arguments, checks, tiles, loads, launch and fold count; every quant byte
+ * (weight and activation) is read as an OCP E4M3FN code and multiplied on the
+ * fp8 matrix cores with f32 accumulation:
+ *   y[t][r] = sum_b d_w[r][b] * d_x[t][b] * sum_i e4m3(q_w) * e4m3(q_x).
+ * Bytes of magnitude 0x7F (e4m3 NaN) give NaN outputs; the instrument's
+ * data avoids them.  Its output is compared only with its own definition;
+ * the pair (this, bqm_q8_0_gemm) prices the accumulator by time.
+ */
+int bqm_q8_0_gemm_f8acc(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds,
+                        float *y, int m, int k, int n, void *stream);
+
+/*
  * Per-batch e4m3 activation quantization ("fp8_ffi.rs" module doc: f32 ->
  * e4m3 with one per-batch scalar scale amax/448, device amax reduce, the
  * scale folded with weight_scale into a device scalar, no host sync;

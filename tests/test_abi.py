@@ -32,7 +32,8 @@ def declared_symbols():
 def test_header_declares_the_calls_and_strerror():
     assert declared_symbols() == sorted([
         "bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax", "bqm_e4m3_gemm",
-        "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm", "bqm_strerror"])
+        "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm", "bqm_q8_0_gemm_f8acc",
+        "bqm_strerror"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -71,7 +72,7 @@ def test_q8_1_quantize_validation(L):
     assert f(A16, B16, MIS2, 1, 32, NUL) == 2
 
 
-@pytest.mark.parametrize("fn", ["bqm_q8_0_gemv", "bqm_q8_0_gemm"])
+@pytest.mark.parametrize("fn", ["bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_q8_0_gemm_f8acc"])
 def test_q8_0_validation(L, fn):
     f = getattr(L, fn)
     rb = 4096 // 32 * 34
