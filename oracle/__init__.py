@@ -62,6 +62,11 @@ def _load():
         lib.oracle_f16_gemm.argtypes = [P, P, I, I, I, P, P]
         lib.oracle_e4m3_gemv_sampled.argtypes = [P, P, ctypes.c_float, I, I, P, P, P, P]
         lib.oracle_q8_0_matmul_e4m3.argtypes = [P, I, P, P, I, I, I, P, P]
+        lib.oracle_e4m3_nan_count.argtypes = [P, I]
+        lib.oracle_e4m3_nan_count.restype = ctypes.c_uint64
+        lib.oracle_e4m3_blk_quantize.argtypes = [P, I, I, P, P]
+        lib.oracle_e4m3_blk_matmul.argtypes = [P, P, P, P, I, I, I, P, P]
+        lib.oracle_e4m3_blk_matmul_sampled.argtypes = [P, P, P, P, I, I, P, P, P, P]
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -244,4 +249,49 @@ def q8_0_matmul_e4m3(w: np.ndarray, xq: np.ndarray, xds: np.ndarray, k: int):
     y = np.empty((m, n), dtype=np.float64)
     T = np.empty((m, n), dtype=np.float64)
     _load().oracle_q8_0_matmul_e4m3(_p(w), w.shape[1], _p(xq), _p(xds), m, k, n, _p(y), _p(T))
+    return y, T
+
+
+def e4m3_nan_count(b: np.ndarray) -> int:
+    """Number of e4m3 NaN codes (magnitude 0x7F) in a byte array."""
+    b = _c(b, np.uint8)
+    return int(_load().oracle_e4m3_nan_count(_p(b), b.size))
+
+
+def e4m3_blk_quantize(x: np.ndarray):
+    """Per (token, 128-k block) e4m3 quantization: (xq uint8 [m, k], xs f32 [m, ceil(k/128)])."""
+    x = _c(x, np.float32)
+    m, k = x.shape
+    xq = np.empty((m, k), dtype=np.uint8)
+    xs = np.empty((m, (k + 127) // 128), dtype=np.float32)
+    _load().oracle_e4m3_blk_quantize(_p(x), m, k, _p(xq), _p(xs))
+    return xq, xs
+
+
+def e4m3_blk_matmul(w: np.ndarray, grid: np.ndarray, xq: np.ndarray, xs: np.ndarray):
+    """Block-128 FP8 matmul in fp64: (y [m, n], sum|terms| [m, n])."""
+    w = _c(w, np.uint8)
+    grid = _c(grid, np.float32)
+    xq = _c(xq, np.uint8)
+    xs = _c(xs, np.float32)
+    n, k = w.shape
+    m = xq.shape[0]
+    assert grid.shape == ((n + 127) // 128, (k + 127) // 128) and xs.shape == (m, (k + 127) // 128)
+    y = np.empty((m, n), dtype=np.float64)
+    T = np.empty((m, n), dtype=np.float64)
+    _load().oracle_e4m3_blk_matmul(_p(w), _p(grid), _p(xq), _p(xs), m, k, n, _p(y), _p(T))
+    return y, T
+
+
+def e4m3_blk_matmul_sampled(w, grid, xq, xs, tok, row):
+    w = _c(w, np.uint8)
+    grid = _c(grid, np.float32)
+    xq = _c(xq, np.uint8)
+    xs = _c(xs, np.float32)
+    tok = _c(tok, np.int64)
+    row = _c(row, np.int64)
+    y = np.empty(len(tok), dtype=np.float64)
+    T = np.empty(len(tok), dtype=np.float64)
+    _load().oracle_e4m3_blk_matmul_sampled(_p(w), _p(grid), _p(xq), _p(xs), w.shape[1], len(tok), _p(tok), _p(row),
+                                           _p(y), _p(T))
     return y, T

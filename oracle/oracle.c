@@ -471,3 +471,97 @@ void oracle_q8_0_matmul_e4m3(const uint8_t *w, int64_t row_bytes, const uint8_t 
         for (int64_t t = 0; t < m; t++)
             q8_0_e4m3_dot(w + r * row_bytes, xq + t * k, xds + t * nb * 2, nb, &y[t * n + r], &tabs[t * n + r]);
 }
+
+/*
+ * Block-128 FP8 operands ("fp8_ffi.rs" page, memra-engine 0.70.0, the
+ * per-block FP8 MMQ section: try_fp8_blk_mmq, fp8_mmq_enabled and the
+ * FP8_MMQ_NAN_OK docs; "accprobe_bench.rs" module doc: the per-block kernel
+ * chains its k32 products into one accumulator and folds once per 128-k
+ * block).  The weight is e4m3 codes [n][k] with a row-major f32 grid
+ * [ceil(n/128)][ceil(k/128)], one scale per 128x128 block, and a per-tensor
+ * scale of 1.  Magnitude 0x7F is NaN to the hardware, so a weight holding
+ * one is refused after a one-time count.
+ *
+ * The pages do not show the activation side of this kernel.  Reading: the
+ * f32 activation is quantized to e4m3 per (token, 128-k block) with the
+ * pages' activation rule, scale amax/448 and multiplier 448/amax (f32
+ * divisions), values scaled in f32, clamped to +-448, rounded to nearest
+ * even; a block whose amax is 0 gets multiplier and scale 0.  A trailing
+ * block shorter than 128 (k % 128 != 0) is quantized over the values it has.
+ */
+uint64_t oracle_e4m3_nan_count(const uint8_t *b, int64_t count) {
+    uint64_t c = 0;
+    for (int64_t i = 0; i < count; i++)
+        if ((b[i] & 0x7F) == 0x7F) c++;
+    return c;
+}
+
+/* xq [m][k] codes, xs [m][ceil(k/128)] scales amax/448. */
+void oracle_e4m3_blk_quantize(const float *x, int64_t m, int64_t k, uint8_t *xq, float *xs) {
+    int64_t kbn = (k + 127) / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < m; t++) {
+        for (int64_t kb = 0; kb < kbn; kb++) {
+            int64_t k0 = kb * 128, k1 = k0 + 128 < k ? k0 + 128 : k;
+            float amax = 0.0f;
+            for (int64_t i = k0; i < k1; i++) {
+                float a = fabsf(x[t * k + i]);
+                if (a > amax) amax = a;
+            }
+            float mul = 0.0f, s = 0.0f;
+            if (amax > 0.0f) {
+                mul = 448.0f / amax;
+                s = amax / 448.0f;
+            }
+            for (int64_t i = k0; i < k1; i++) xq[t * k + i] = oracle_e4m3_encode(x[t * k + i] * mul);
+            xs[t * kbn + kb] = s;
+        }
+    }
+}
+
+/*
+ * y[t][r] = sum_kb grid[r/128][kb] * xs[t][kb] * sum_{i in kb} dec(xq[t][i]) * dec(w[r][i]),
+ * fp64: each block's e4m3 product sum is exact, then one fp64 rounding per
+ * block term.  tabs = sum_kb |grid * xs| * sum_i |dec * dec|.
+ */
+static void e4m3_blk_dot(const uint8_t *wrow, const float *grow, const uint8_t *xrow, const float *xsrow,
+                         int64_t k, double *y, double *tabs) {
+    int64_t kbn = (k + 127) / 128;
+    double acc = 0.0, aabs = 0.0;
+    for (int64_t kb = 0; kb < kbn; kb++) {
+        int64_t k0 = kb * 128, k1 = k0 + 128 < k ? k0 + 128 : k;
+        double s = 0.0, sabs = 0.0;
+        for (int64_t i = k0; i < k1; i++) {
+            double p = e4m3_table[xrow[i]] * e4m3_table[wrow[i]];
+            s += p;
+            sabs += fabs(p);
+        }
+        double scale = (double)grow[kb] * (double)xsrow[kb];
+        acc += scale * s;
+        aabs += fabs(scale) * sabs;
+    }
+    *y = acc;
+    *tabs = aabs;
+}
+
+void oracle_e4m3_blk_matmul(const uint8_t *w, const float *grid, const uint8_t *xq, const float *xs, int64_t m,
+                            int64_t k, int64_t n, double *y, double *tabs) {
+    int64_t kbn = (k + 127) / 128;
+    e4m3_fill_table();
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t t = 0; t < m; t++)
+            e4m3_blk_dot(w + r * k, grid + (r / 128) * kbn, xq + t * k, xs + t * kbn, k, &y[t * n + r],
+                         &tabs[t * n + r]);
+}
+
+void oracle_e4m3_blk_matmul_sampled(const uint8_t *w, const float *grid, const uint8_t *xq, const float *xs,
+                                    int64_t k, int64_t npairs, const int64_t *tok, const int64_t *row, double *y,
+                                    double *tabs) {
+    int64_t kbn = (k + 127) / 128;
+    e4m3_fill_table();
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npairs; p++)
+        e4m3_blk_dot(w + row[p] * k, grid + (row[p] / 128) * kbn, xq + tok[p] * k, xs + tok[p] * kbn, k, &y[p],
+                     &tabs[p]);
+}

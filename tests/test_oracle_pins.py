@@ -569,3 +569,87 @@ def test_accprobe_bytes_are_finite_in_both_readings(dist):
         assert np.all(np.isfinite(_torch_e4m3(b)))
     if dist == "wide":
         assert len(np.unique(q)) == 252
+
+
+# --------------------------------------------------------------------------- block-128 FP8
+
+
+def test_e4m3_nan_count_matches_numpy_and_torch():
+    rng = np.random.default_rng(21)
+    b = rng.integers(0, 256, size=100003, dtype=np.uint8)
+    want = int(np.count_nonzero((b & 0x7F) == 0x7F))
+    assert want > 0
+    assert oracle.e4m3_nan_count(b) == want
+    assert oracle.e4m3_nan_count(b) == int(np.isnan(_torch_e4m3(b)).sum())
+    clean = np.where((b & 0x7F) == 0x7F, b & 0x80, b).astype(np.uint8)
+    assert oracle.e4m3_nan_count(clean) == 0
+
+
+@pytest.mark.parametrize("m,k", [(3, 256), (5, 200), (2, 4096)])
+def test_e4m3_blk_quantize_matches_torch_cast_per_block(m, k):
+    rng = np.random.default_rng(m + k)
+    x = workloads.activations(m, k, rng, outliers=True)
+    x[0, :min(k, 128)] = 0.0                                  # an all-zero block
+    if m > 1:
+        x[1, -1] = -0.0
+    xq, xs = oracle.e4m3_blk_quantize(x)
+    kbn = (k + 127) // 128
+    assert xs.shape == (m, kbn)
+    for t in range(m):
+        for kb in range(kbn):
+            blk = x[t, 128 * kb:128 * kb + 128]
+            amax = np.float32(np.abs(blk).max())
+            if amax == 0:
+                assert xs[t, kb] == 0
+                assert np.all((xq[t, 128 * kb:128 * kb + 128] & 0x7F) == 0)
+                continue
+            mul = np.float32(448.0) / amax
+            assert xs[t, kb] == amax / np.float32(448.0)
+            v = np.clip(blk * mul, np.float32(-448.0), np.float32(448.0)).astype(np.float32)
+            ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(xq[t, 128 * kb:128 * kb + 128], ref)
+
+
+def test_e4m3_blk_quantize_closed_forms():
+    x = np.full((1, 256), 3.0, np.float32)
+    x[0, 128:] = -0.5
+    xq, xs = oracle.e4m3_blk_quantize(x)
+    assert np.all(xq[0, :128] == 0x7E) and np.all(xq[0, 128:] == 0xFE)
+    assert xs[0, 0] == np.float32(3.0) / np.float32(448.0) and xs[0, 1] == np.float32(0.5) / np.float32(448.0)
+
+
+def test_e4m3_blk_matmul_matches_fp64_of_torch_decoded_blocks():
+    rng = np.random.default_rng(8)
+    n, k, m = 300, 640, 7
+    w, grid = workloads.e4m3_blk_weights(n, k, rng)
+    xq, xs = oracle.e4m3_blk_quantize(workloads.activations(m, k, rng))
+    y, T = oracle.e4m3_blk_matmul(w, grid, xq, xs)
+    W = _torch_e4m3(w) * np.repeat(np.repeat(grid.astype(np.float64), 128, 0), 128, 1)[:n, :k]
+    X = _torch_e4m3(xq) * np.repeat(xs.astype(np.float64), 128, 1)[:, :k]
+    assert np.all(np.abs(y - X @ W.T) <= 1e-12 * T)
+    assert np.allclose(T, np.abs(X) @ np.abs(W).T, rtol=1e-12, atol=0)
+    # the sampled form gives the same numbers
+    tok = np.array([0, 6, 3]); row = np.array([299, 0, 128])
+    ys, Ts = oracle.e4m3_blk_matmul_sampled(w, grid, xq, xs, tok, row)
+    assert np.array_equal(ys, y[tok, row]) and np.array_equal(Ts, T[tok, row])
+
+
+def test_e4m3_blk_matmul_one_hot_and_closed_form():
+    rng = np.random.default_rng(9)
+    n, k = 200, 384
+    w, grid = workloads.e4m3_blk_weights(n, k, rng)
+    xq = np.zeros((2, k), np.uint8)
+    xq[0, 5] = 0x38                                        # 1.0 in block 0
+    xq[1, 300] = 0xB8                                      # -1.0 in block 2
+    xs = np.array([[1.0, 1.0, 1.0], [1.0, 1.0, 0.25]], np.float32)
+    y, _ = oracle.e4m3_blk_matmul(w, grid, xq, xs)
+    wd = _torch_e4m3(w)
+    rb = np.arange(n) // 128
+    assert np.array_equal(y[0], grid[rb, 0].astype(np.float64) * wd[:, 5])
+    assert np.array_equal(y[1], -0.25 * grid[rb, 2].astype(np.float64) * wd[:, 300])
+    wc = np.full((3, 256), 0x44, np.uint8)                 # 3.0
+    gc = np.full((1, 2), 0.5, np.float32)
+    xc = np.full((2, 256), 0xC5, np.uint8)                 # -3.25
+    xsc = np.full((2, 2), 0.125, np.float32)
+    yc, Tc = oracle.e4m3_blk_matmul(wc, gc, xc, xsc)
+    assert np.all(yc == 256 * 3.0 * -3.25 * 0.5 * 0.125) and np.all(Tc == -yc)

@@ -26,6 +26,12 @@ Draw order per call (fixed; changing it changes every workload):
 ``e4m3_weights``: ``normal(0, 0.02, (N, K))``; the per-tensor scale is
 ``max|w| / 448`` and the codes are torch's ``float8_e4m3fn`` cast of
 ``w / scale`` (a library conversion, not this project's encoder).
+``e4m3_blk_weights``: ``normal(0, 0.02, (N, K))``; the grid holds each
+128x128 block's ``max|w| / 448`` (f32) and the codes are torch's
+``float8_e4m3fn`` cast of ``w`` divided by its block's scale, clamped to
++-448 (the block-128 FP8 checkpoint format of the "fp8_ffi.rs" page's
+per-block MMQ section: e4m3 codes plus a row-major f32 grid
+``[ceil(N/128)][ceil(K/128)]``).
 ``accprobe_weights`` / ``accprobe_activations`` (the accumulator
 instrument's quantizer-free bytes, "accprobe_bench.rs" page (memra-engine
 0.124.1), fns ``synth_w_q8_0`` and ``synth_act_q8_1``: quant magnitudes at
@@ -99,6 +105,21 @@ def e4m3_weights(n: int, k: int, rng: np.random.Generator):
     v = np.clip(w / w_scale, -448.0, 448.0).astype(np.float32)
     codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
     return codes, float(w_scale)
+
+
+def e4m3_blk_weights(n: int, k: int, rng: np.random.Generator):
+    """Block-128 FP8 weights from N(0, 0.02): (codes uint8 [n, k], grid f32 [ceil(n/128), ceil(k/128)])."""
+    import torch
+
+    w = rng.normal(0.0, 0.02, size=(n, k)).astype(np.float32)
+    nb, kb = (n + 127) // 128, (k + 127) // 128
+    pad = np.zeros((nb * 128, kb * 128), np.float32)
+    pad[:n, :k] = np.abs(w)
+    grid = (pad.reshape(nb, 128, kb, 128).max(axis=(1, 3)) / np.float32(448.0)).astype(np.float32)
+    g = np.repeat(np.repeat(grid, 128, axis=0), 128, axis=1)[:n, :k]
+    v = np.clip(w / g, -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, grid
 
 
 def _accprobe_quants(rows: int, k: int, rng: np.random.Generator, dist: str) -> np.ndarray:
