@@ -14,7 +14,9 @@ and the FP8-E4M3 GEMM (amax quantize + fp8 GEMM) at N=20480, with int8/fp8
 TOPS and their fraction of the matrix-core peak; the e4m3 decode GEMV
 (raw e4m3 weights, f32 activations) at m=1 and 9 on the head shape; the fp16
 mirror prefill (f32 -> fp16 cast + fp16 GEMM, m=512, K=4096, N=20480, with the
-one-off Q8_0 -> fp16 dequant timed beside it); the accumulator instrument
+one-off Q8_0 -> fp16 dequant timed beside it); the block-128 FP8 prefill
+(per-(token, 128-k block) e4m3 quantize + per-block GEMM, m=512, K=4096,
+N=20480, with the one-off NaN scan of the weight); the accumulator instrument
 (the MMQ with its int8 MFMA + s32 block sums against the same kernel with
 fp8 MFMAs + f32 block sums, m=512, the 27B projection shapes, both arms timed
 interleaved per rep, medians, geomean of the ratio); a roofline object for the
@@ -111,7 +113,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3", "e4m3_gemv", "f16", "accprobe", "copy"], default=None,
+    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3", "e4m3_gemv", "f16", "accprobe", "e4m3_blk", "copy"], default=None,
                     help="run one part only (for profiler passes); 'copy' runs a plain 1 GiB device copy "
                          "that calibrates the HBM byte counters")
     args = ap.parse_args()
@@ -286,6 +288,40 @@ def main():
             "dequant_us": round(per_dq["dequant"] * 1e3, 2),
             "dequant_gbs": round(dq_bytes / (per_dq["dequant"] * 1e-3) / 1e9, 1)}
         del w16s, wq, y
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- block-128 FP8 prefill
+    if args.only in (None, "e4m3_blk"):
+        m, k, n = 512, 4096, 20480
+        log("[bench] e4m3 block-128 n=20480")
+        codes, grid_h = workloads.e4m3_blk_weights(n, k, rng)
+        w0 = torch.from_numpy(codes).to(dev)
+        ws = [w0] + [w0.clone() for _ in range(ROTATE - 1)]
+        grid = torch.from_numpy(grid_h).to(dev)
+        x = torch.from_numpy(workloads.activations(m, k, rng, outliers=True)).to(dev)
+        xq8 = torch.empty((m, k), dtype=torch.uint8, device=dev)
+        xs = torch.empty((m, k // 128), dtype=torch.float32, device=dev)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        fns = [("quantize", lambda s: bqm.bqm_e4m3_blk_quantize(x, xq8, xs)),
+               ("gemm", lambda s: bqm.bqm_e4m3_blk_gemm(ws[s % ROTATE], grid, xq8, xs, y))]
+        timed_loop(torch, stream, args.warmup, fns)
+        total_ms, per = timed_loop(torch, stream, args.steps, fns)
+        cnt = torch.empty(1, dtype=torch.int64, device=dev)
+        scan = [("nan_scan", lambda s: bqm.bqm_e4m3_nan_count(ws[s % ROTATE], cnt))]
+        timed_loop(torch, stream, 2, scan)
+        _, per_scan = timed_loop(torch, stream, args.steps, scan)
+        ops = 2.0 * m * n * k
+        tf = ops / (per["gemm"] * 1e-3) / 1e12
+        out["e4m3_blk_m512"] = {
+            "workload": "block-128 FP8 GEMM m=512, K=4096, N=20480: per-(token, 128-k) e4m3 activations, "
+                        "per-128x128 f32 weight grid, one fold per 128-k block",
+            "gemm_us": round(per["gemm"] * 1e3, 2), "quantize_us": round(per["quantize"] * 1e3, 2),
+            "tflops": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+            "step_tflops": round(ops / (total_ms / args.steps * 1e-3) / 1e12, 1),
+            "nan_scan_us": round(per_scan["nan_scan"] * 1e3, 2),
+            "nan_scan_gbs": round(n * k / (per_scan["nan_scan"] * 1e-3) / 1e9, 1),
+            "nan_codes": int(cnt.item())}
+        del ws, w0, y
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- accumulator instrument

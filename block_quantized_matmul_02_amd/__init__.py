@@ -43,6 +43,9 @@ def lib() -> ctypes.CDLL:
         L.bqm_q8_0_gemv.argtypes = [P, I64, P, P, P, I, I, I, P]
         L.bqm_q8_0_gemm.argtypes = [P, I64, P, P, P, I, I, I, P]
         L.bqm_q8_0_gemm_f8acc.argtypes = [P, I64, P, P, P, I, I, I, P]
+        L.bqm_e4m3_nan_count.argtypes = [P, I64, P, P]
+        L.bqm_e4m3_blk_quantize.argtypes = [P, P, P, I, I, P]
+        L.bqm_e4m3_blk_gemm.argtypes = [P, P, P, P, P, I, I, I, P]
         L.bqm_e4m3_quantize_amax.argtypes = [P, P, P, F, I, I, P]
         L.bqm_e4m3_gemm.argtypes = [P, P, P, P, I, I, I, P]
         L.bqm_e4m3_gemv.argtypes = [P, P, F, P, I, I, I, P]
@@ -50,7 +53,8 @@ def lib() -> ctypes.CDLL:
         L.bqm_f16_cvt.argtypes = [P, P, I64, P]
         L.bqm_f16_gemm.argtypes = [P, P, P, I, I, I, P]
         for fn in ("bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax",
-                   "bqm_e4m3_gemm", "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm", "bqm_q8_0_gemm_f8acc"):
+                   "bqm_e4m3_gemm", "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm",
+                   "bqm_q8_0_gemm_f8acc", "bqm_e4m3_nan_count", "bqm_e4m3_blk_quantize", "bqm_e4m3_blk_gemm"):
             getattr(L, fn).restype = ctypes.c_int
         L.bqm_strerror.argtypes = [I]
         L.bqm_strerror.restype = ctypes.c_char_p
@@ -238,4 +242,51 @@ def bqm_f16_gemm(w16, x16, y=None):
         y = torch.empty((m, n), dtype=torch.float32, device=x16.device)
     _check(y, torch.float32, "y", (m, n))
     _raise("bqm_f16_gemm", lib().bqm_f16_gemm(_ptr(w16), _ptr(x16), _ptr(y), m, k, n, _stream(w16)))
+    return y
+
+
+def bqm_e4m3_nan_count(w, out=None):
+    """Number of e4m3 NaN codes (magnitude 0x7F) in a uint8 tensor, as a device int64 tensor of one element."""
+    import torch
+
+    _check(w, torch.uint8, "w")
+    if out is None:
+        out = torch.empty(1, dtype=torch.int64, device=w.device)
+    _check(out, torch.int64, "out", (1,))
+    _raise("bqm_e4m3_nan_count", lib().bqm_e4m3_nan_count(_ptr(w), w.numel(), _ptr(out), _stream(w)))
+    return out
+
+
+def bqm_e4m3_blk_quantize(x, xq=None, xs=None):
+    """Per (token, 128-k block) e4m3 quantization of f32 ``x [m, k]`` -> (uint8 ``xq [m, k]``, f32 ``xs [m, k/128]``)."""
+    import torch
+
+    m, k = x.shape
+    _check(x, torch.float32, "x")
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if xs is None:
+        xs = torch.empty((m, k // 128), dtype=torch.float32, device=x.device)
+    _check(xq, torch.uint8, "xq", (m, k))
+    _check(xs, torch.float32, "xs", (m, k // 128))
+    _raise("bqm_e4m3_blk_quantize", lib().bqm_e4m3_blk_quantize(_ptr(x), _ptr(xq), _ptr(xs), m, k, _stream(x)))
+    return xq, xs
+
+
+def bqm_e4m3_blk_gemm(w, grid, xq, xs, y=None):
+    """Block-128 FP8 GEMM: e4m3 ``w [n, k]`` with f32 ``grid [ceil(n/128), k/128]``, ``xq``/``xs`` from
+    bqm_e4m3_blk_quantize -> f32 ``y [m, n]``."""
+    import torch
+
+    n, k = w.shape
+    m = xq.shape[0]
+    _check(w, torch.uint8, "w")
+    _check(grid, torch.float32, "grid", ((n + 127) // 128, k // 128))
+    _check(xq, torch.uint8, "xq", (m, k))
+    _check(xs, torch.float32, "xs", (m, k // 128))
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _check(y, torch.float32, "y", (m, n))
+    _raise("bqm_e4m3_blk_gemm", lib().bqm_e4m3_blk_gemm(_ptr(w), _ptr(grid), _ptr(xq), _ptr(xs), _ptr(y), m, k, n,
+                                                        _stream(w)))
     return y

@@ -1,0 +1,341 @@
+// Block-128 FP8 prefill path for gfx950: the e4m3 NaN-code count of a weight,
+// the per-(token, 128-k block) activation quantization, and the per-block FP8
+// GEMM that folds once per 128-k block.
+//
+// From the "fp8_ffi.rs" page (memra-engine 0.70.0), the per-block FP8 MMQ
+// section (try_fp8_blk_mmq, fp8_mmq_enabled and FP8_MMQ_NAN_OK docs): the
+// weight is the checkpoint's e4m3 codes [n][k] with a row-major f32 grid
+// [ceil(n/128)][ceil(k/128)], one scale per 128x128 block, and no second
+// (per-tensor) scale; the hardware reads magnitude 0x7F as NaN, so a weight
+// holding any is refused after a one-time count; y[m,out] = x[m,in] @ W^T with
+// each weight block scaled by its own f32.  The "accprobe_bench.rs" module
+// doc describes the kernel class: products chained into one accumulator per
+// 128-k block and folded once per block.  The activation side is not shown on
+// the pages; it is quantized here per (token, 128-k block) with the pages'
+// amax/448 rule, so block kb of output (t, r) folds by grid[r/128][kb] *
+// xs[t][kb].
+//
+// GEMM design (MFMA-bound, one fold per 128-k block):
+//  * The e4m3 GEMM's organisation: workgroup tile 128 x 64*NT, 8 waves of
+//    32 x 32*NT (two per SIMD), k staged 128 at a time (exactly one grid
+//    block) in double-buffered LDS with padded 144-byte rows, global loads
+//    two stages ahead in registers.
+//  * Per stage a wave runs two v_mfma_scale_f32_32x32x64_f8f6f4 (unit E8M0
+//    scales) per 32x32 tile into a block partial P started at zero, then
+//    folds acc += P * (xs[t] * g), two VALU ops per output element.  g is one
+//    scalar per 32-column tile (a 32-aligned tile never straddles a 128-row
+//    block of the grid), read with scalar loads one stage ahead; the 128
+//    token scales of the stage go through LDS with the operand tiles.
+#include "bqmm_internal.h"
+
+namespace bqm {
+
+// ------------------------------------------------------------------ NaN count
+
+// Bytes whose low 7 bits are all ones, counted per dword without branches:
+// t is zero exactly in those bytes, and the high bit of each byte of the
+// final mask is set exactly where t's byte is zero (no carries cross bytes).
+__device__ __forceinline__ unsigned nan_bytes(unsigned d) {
+    const unsigned t = (d & 0x7F7F7F7Fu) ^ 0x7F7F7F7Fu;
+    const unsigned y = (t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
+    return (unsigned)__builtin_popcount(~(y | t | 0x7F7F7F7Fu));
+}
+
+__global__ void e4m3_nan_zero_kernel(unsigned long long *out) {
+    if (threadIdx.x == 0) *out = 0ull;
+}
+
+__global__ __launch_bounds__(256) void e4m3_nan_count_kernel(const u32x4 *__restrict__ b, int64_t nvec,
+                                                             const uint8_t *__restrict__ bytes, int64_t count,
+                                                             unsigned long long *out) {
+    __shared__ unsigned part[4];
+    unsigned c = 0;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride) {
+        const u32x4 v = __builtin_nontemporal_load(b + i);
+        c += nan_bytes(v[0]) + nan_bytes(v[1]) + nan_bytes(v[2]) + nan_bytes(v[3]);
+    }
+    // the count % 16 tail, one byte per thread of the first workgroup
+    if (blockIdx.x == 0) {
+        const int64_t t = nvec * 16 + threadIdx.x;
+        if (t < count) c += ((bytes[t] & 0x7F) == 0x7F) ? 1u : 0u;
+    }
+    // wave sums: DPP within rows of 16, then the row and half exchanges
+    c += (unsigned)__builtin_amdgcn_update_dpp(0, (int)c, 0xB1, 0xF, 0xF, false);
+    c += (unsigned)__builtin_amdgcn_update_dpp(0, (int)c, 0x4E, 0xF, 0xF, false);
+    c += (unsigned)__builtin_amdgcn_update_dpp(0, (int)c, 0x141, 0xF, 0xF, false);
+    c += (unsigned)__builtin_amdgcn_update_dpp(0, (int)c, 0x140, 0xF, 0xF, false);
+    {
+        auto s = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+        unsigned a0 = s[0], a1 = s[1];
+        c = a0 + a1;
+        auto s2 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+        unsigned b0 = s2[0], b1 = s2[1];
+        c = b0 + b1;
+    }
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned long long total = (unsigned long long)part[0] + part[1] + part[2] + part[3];
+        if (total) atomicAdd(out, total);
+    }
+}
+
+// ------------------------------------------------------------------ activation quantization
+
+__device__ __forceinline__ float dpp_max16(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
+__device__ __forceinline__ float clamp448b(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// One 128-value block per 32 lanes (a float4 each), eight blocks per
+// workgroup.  Blocks are numbered t * (k/128) + kb, the order of x and of xs.
+__global__ __launch_bounds__(256) void e4m3_blk_quantize_kernel(const float4 *__restrict__ x, int64_t nblocks,
+                                                                unsigned *__restrict__ xq, float *__restrict__ xs) {
+    const int64_t g0 = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+    const bool live = g0 < nblocks;
+    const int64_t g = live ? g0 : nblocks - 1;   // past the end: recompute the last block, store nothing
+    const int l = threadIdx.x & 31;
+    const float4 v = x[g * 32 + l];
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    a = dpp_max16(a);
+    a = swap16_max(a);   // lanes l and l^16: the block's 32 lanes
+    float mul = 0.0f, s = 0.0f;
+    if (a > 0.0f) {
+        mul = 448.0f / a;
+        s = a / 448.0f;
+    }
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448b(v.x * mul), clamp448b(v.y * mul), 0, false);
+    const int both = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448b(v.z * mul), clamp448b(v.w * mul), lo, true);
+    if (live) {
+        xq[g * 32 + l] = (unsigned)both;
+        if (l == 0) xs[g] = s;
+    }
+}
+
+// ------------------------------------------------------------------ GEMM
+
+constexpr int kB8BM = 128;                 // workgroup tile rows (tokens)
+constexpr int kB8KB = 128;                 // k per stage = one grid block
+constexpr int kB8Threads = 512;            // 8 waves, 4 x 2
+constexpr int kB8RowStride = kB8KB + 16;   // 144: padded LDS row
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t b8_rsrc(const void *base, int64_t bytes) {
+    uint32_t b = bytes <= 0 ? 0u : (bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0u : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)b, 0x00020000);
+}
+
+template <int NT>
+struct B8Stage {
+    uint8_t a[kB8BM * kB8RowStride];
+    uint8_t b[64 * NT * kB8RowStride];
+    float xs[kB8Threads];    // token scale of row (i & 127), written by every thread
+};
+
+template <int NT>
+struct B8Regs {
+    u32x4 a[2];        // 128 rows x 128 bytes = 1024 chunks, 2 per thread
+    u32x4 b[NT];       // 64*NT rows x 128 bytes, NT per thread
+    float xs;          // the token scale of row (tid & 127)
+    float g[NT];       // grid scale of each 32-column tile of this wave (uniform)
+};
+
+template <int NT>
+__global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t *__restrict__ w,
+                                                                 const float *__restrict__ grid,
+                                                                 const uint8_t *__restrict__ xq,
+                                                                 const float *__restrict__ xs,
+                                                                 float *__restrict__ y, int m, int k, int n) {
+    constexpr int BN = 64 * NT;
+    __shared__ __attribute__((aligned(16))) B8Stage<NT> st[2];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int n0 = blockIdx.x * BN;
+    const int m0 = blockIdx.y * kB8BM;
+    const int nstage = k / kB8KB;        // = k/128 grid columns
+    const int nbn = (n + 127) / 128;     // grid rows
+
+    const __amdgpu_buffer_rsrc_t rA = b8_rsrc(xq + (int64_t)m0 * k, (int64_t)(m - m0) * k);
+    const __amdgpu_buffer_rsrc_t rB = b8_rsrc(w + (int64_t)n0 * k, (int64_t)(n - n0) * k);
+    const __amdgpu_buffer_rsrc_t rS = b8_rsrc(xs + (int64_t)m0 * nstage, (int64_t)(m - m0) * nstage * 4);
+
+    // grid rows of this wave's 32-column tiles; a tile past n reads the last
+    // grid row (its outputs are not stored)
+    const float *gcol[NT];
+#pragma unroll
+    for (int j = 0; j < NT; j++) {
+        const int cb = min((n0 + wn * 32 * NT + 32 * j) >> 7, nbn - 1);
+        gcol[j] = grid + (int64_t)cb * nstage;
+    }
+
+    const uint32_t goff = (uint32_t)((tid >> 3) * k + 16 * (tid & 7));
+    const uint32_t grow64 = (uint32_t)(64 * k);
+    const uint32_t soff = (uint32_t)((tid & 127) * nstage * 4);
+    auto load_stage = [&](B8Regs<NT> &R, int kc) {
+        const int so = kc * kB8KB;
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+            R.a[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, goff + s * grow64, so, 0));
+#pragma unroll
+        for (int s = 0; s < NT; s++)
+            R.b[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, goff + s * grow64, so, 0));
+        R.xs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, soff, kc * 4, 0));
+#pragma unroll
+        for (int j = 0; j < NT; j++) R.g[j] = gcol[j][kc];
+    };
+    const int lds_off = (tid >> 3) * kB8RowStride + 16 * (tid & 7);
+    float G0[NT], G1[NT];   // grid scales of the stage held in st[0] / st[1]
+    auto store_stage = [&](B8Stage<NT> &S, const B8Regs<NT> &R, float (&G)[NT]) {
+#pragma unroll
+        for (int s = 0; s < 2; s++)
+            *reinterpret_cast<u32x4 *>(S.a + lds_off + s * 64 * kB8RowStride) = R.a[s];
+#pragma unroll
+        for (int s = 0; s < NT; s++)
+            *reinterpret_cast<u32x4 *>(S.b + lds_off + s * 64 * kB8RowStride) = R.b[s];
+        S.xs[tid] = R.xs;
+#pragma unroll
+        for (int j = 0; j < NT; j++) G[j] = R.g[j];
+    };
+
+    v16f acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; j++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[j][v] = 0.0f;
+
+    const int khalf = lane >> 5;
+    // Lane l supplies row l%32 of each 32-row operand tile and k values
+    // 32*(l/32) .. +31 of the 64-deep step (the same k set for A and B).
+    auto compute_stage = [&](const B8Stage<NT> &S, const float (&G)[NT]) {
+        const uint8_t *pa = S.a + (wm * 32 + (lane & 31)) * kB8RowStride + 32 * khalf;
+        const uint8_t *pb = S.b + (wn * 32 * NT + (lane & 31)) * kB8RowStride + 32 * khalf;
+        auto ld8 = [](const uint8_t *p) {
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(p);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + 16);
+            return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        };
+        v8i a0 = ld8(pa), a1 = ld8(pa + 64);
+        v8i b0[NT], b1[NT];
+#pragma unroll
+        for (int j = 0; j < NT; j++) {
+            b0[j] = ld8(pb + j * 32 * kB8RowStride);
+            b1[j] = ld8(pb + j * 32 * kB8RowStride + 64);
+        }
+        v16f P[NT];
+        const v16f z = {0};
+#pragma unroll
+        for (int j = 0; j < NT; j++)
+            P[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0[j], z, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int j = 0; j < NT; j++)
+            P[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1[j], P[j], 0, 0, 0, 127, 0, 127);
+        // token scales of the 16 output rows of this lane: rows
+        // wm*32 + 8*(v/4) + 4*khalf + v%4, four consecutive per float4
+        float sx[16];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float4 q = *reinterpret_cast<const float4 *>(S.xs + wm * 32 + 8 * i + 4 * khalf);
+            sx[4 * i + 0] = q.x;
+            sx[4 * i + 1] = q.y;
+            sx[4 * i + 2] = q.z;
+            sx[4 * i + 3] = q.w;
+        }
+#pragma unroll
+        for (int j = 0; j < NT; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[j][v] = __builtin_fmaf(P[j][v], sx[v] * G[j], acc[j][v]);
+    };
+
+    B8Regs<NT> R0, R1;
+    const int last = nstage - 1;
+    load_stage(R0, 0);
+    load_stage(R1, min(1, last));
+    store_stage(st[0], R0, G0);
+    __syncthreads();
+    int kc = 0;
+#pragma unroll 1
+    for (; kc + 1 < nstage; kc += 2) {
+        load_stage(R0, min(kc + 2, last));
+        compute_stage(st[0], G0);
+        store_stage(st[1], R1, G1);
+        __syncthreads();
+        load_stage(R1, min(kc + 3, last));
+        compute_stage(st[1], G1);
+        store_stage(st[0], R0, G0);
+        __syncthreads();
+    }
+    if (kc < nstage) compute_stage(st[0], G0);
+
+#pragma unroll
+    for (int j = 0; j < NT; j++) {
+        const int col = n0 + wn * 32 * NT + j * 32 + (lane & 31);
+        if (col >= n) continue;
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int row = m0 + wm * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+            if (row < m) y[(int64_t)row * n + col] = acc[j][v];
+        }
+    }
+}
+
+template <int NT>
+static int launch_b8(const uint8_t *w, const float *grid, const uint8_t *xq, const float *xs, float *y, int m, int k,
+                     int n, hipStream_t s) {
+    dim3 g((n + 64 * NT - 1) / (64 * NT), (m + kB8BM - 1) / kB8BM);
+    if (g.y > 65535) return BQM_EUNSUPPORTED;
+    hipLaunchKernelGGL(e4m3_blk_gemm_kernel<NT>, g, dim3(kB8Threads), 0, s, w, grid, xq, xs, y, m, k, n);
+    return launch_status();
+}
+
+}  // namespace bqm
+
+extern "C" int bqm_e4m3_nan_count(const uint8_t *w, int64_t count, unsigned long long *nan_count, void *stream) {
+    using namespace bqm;
+    if (!w || !nan_count) return BQM_EINVAL;
+    if (count < 1) return BQM_EINVAL;
+    if (!aligned(w, 16) || !aligned(nan_count, 8)) return BQM_EUNSUPPORTED;
+    hipStream_t s = as_stream(stream);
+    hipLaunchKernelGGL(e4m3_nan_zero_kernel, dim3(1), dim3(64), 0, s, nan_count);
+    int rc = launch_status();
+    if (rc) return rc;
+    const int64_t nvec = count / 16;
+    int64_t blocks = (nvec + 256 * 8 - 1) / (256 * 8);
+    if (blocks > 2048) blocks = 2048;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(e4m3_nan_count_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const u32x4 *>(w), nvec, w, count, nan_count);
+    return launch_status();
+}
+
+extern "C" int bqm_e4m3_blk_quantize(const float *x, uint8_t *xq, float *xs, int m, int k, void *stream) {
+    using namespace bqm;
+    if (!x || !xq || !xs) return BQM_EINVAL;
+    if (m < 1 || k < 128) return BQM_EINVAL;
+    if (k % 128 != 0) return BQM_EUNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(xs, 4)) return BQM_EUNSUPPORTED;
+    const int64_t nblocks = (int64_t)m * (k / 128);
+    const int64_t wgs = (nblocks + 7) / 8;
+    if (wgs > 0x7FFFFFFF) return BQM_EUNSUPPORTED;
+    hipLaunchKernelGGL(e4m3_blk_quantize_kernel, dim3((unsigned)wgs), dim3(256), 0, as_stream(stream),
+                       reinterpret_cast<const float4 *>(x), nblocks, reinterpret_cast<unsigned *>(xq), xs);
+    return launch_status();
+}
+
+extern "C" int bqm_e4m3_blk_gemm(const uint8_t *w, const float *grid, const uint8_t *xq, const float *xs, float *y,
+                                 int m, int k, int n, void *stream) {
+    using namespace bqm;
+    if (!w || !grid || !xq || !xs || !y) return BQM_EINVAL;
+    if (m < 1 || k < 128 || n < 1) return BQM_EINVAL;
+    if (k % 128 != 0) return BQM_EUNSUPPORTED;
+    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(grid, 4) || !aligned(xs, 4) || !aligned(y, 4))
+        return BQM_EUNSUPPORTED;
+    if ((int64_t)kB8BM * k > 0x7FFFFFF0ll || (int64_t)320 * k > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
+    return launch_b8<3>(w, grid, xq, xs, y, m, k, n, as_stream(stream));
+}

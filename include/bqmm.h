@@ -206,6 +206,50 @@ int bqm_f16_cvt(const float *x, uint16_t *x16, int64_t count, void *stream);
 int bqm_f16_gemm(const uint16_t *w16, const uint16_t *x16, float *y, int m, int k, int n,
                  void *stream);
 
+/*
+ * Block-128 FP8 prefill path ("fp8_ffi.rs" page, memra-engine 0.70.0, the
+ * per-block FP8 MMQ section: try_fp8_blk_mmq, fp8_mmq_enabled and
+ * FP8_MMQ_NAN_OK docs).  The weight is the checkpoint's e4m3 codes with a
+ * row-major f32 grid of one scale per 128x128 block and no per-tensor scale;
+ * the kernel folds once per 128-k block ("accprobe_bench.rs" module doc).
+ *
+ * bqm_e4m3_nan_count: *nan_count = number of bytes of w[0..count) whose low
+ * 7 bits are all ones (the e4m3 NaN codes 0x7F / 0xFF, which the matrix cores
+ * read as NaN), meant to run once per weight tensor; a tensor with any must
+ * not go through bqm_e4m3_blk_gemm.
+ *   w         : bytes, 16-byte aligned;  count >= 1 (else BQM_EINVAL).
+ *   nan_count : one device uint64, 8-byte aligned, overwritten (zeroed by a
+ *               kernel on the stream, then accumulated).
+ */
+int bqm_e4m3_nan_count(const uint8_t *w, int64_t count, unsigned long long *nan_count, void *stream);
+
+/*
+ * bqm_e4m3_blk_quantize: per (token t, 128-k block kb) e4m3 quantization of
+ * the f32 activation with the pages' activation rule amax/448:
+ *   amax = max |x[t][128kb .. 128kb+127]|; mul = 448/amax, xs = amax/448 (f32
+ *   divisions; both 0 when amax is 0); xq = e4m3(clamp(x * mul, +-448)),
+ *   round to nearest even, sign of zero kept, NaN codes never produced.
+ *   x  : f32 [m][k], 16-byte aligned.      xq : uint8 [m][k] out, 4-byte aligned.
+ *   xs : f32 [m][k/128] out, 4-byte aligned.
+ *   m >= 1, k >= 128 (else BQM_EINVAL); k % 128 == 0 (else BQM_EUNSUPPORTED).
+ * The pages do not show this kernel's activation side; this is the reading
+ * that gives one fold per 128-k block on both operands.
+ */
+int bqm_e4m3_blk_quantize(const float *x, uint8_t *xq, float *xs, int m, int k, void *stream);
+
+/*
+ * bqm_e4m3_blk_gemm: y[t][r] = sum_kb grid[r/128][kb] * xs[t][kb] *
+ *   sum_{i in kb} e4m3(xq[t][i]) * e4m3(w[r][i]), f32 accumulation, one fold
+ *   per 128-k block.
+ *   w    : e4m3 codes [n][k], 16-byte aligned, free of NaN codes.
+ *   grid : f32 [ceil(n/128)][k/128] row-major, 4-byte aligned.
+ *   xq   : e4m3 codes [m][k], 16-byte aligned;  xs : f32 [m][k/128].
+ *   y    : f32 [m][n] out, fully overwritten.
+ *   m, n >= 1, k >= 128 (else BQM_EINVAL); k % 128 == 0 (else BQM_EUNSUPPORTED).
+ */
+int bqm_e4m3_blk_gemm(const uint8_t *w, const float *grid, const uint8_t *xq, const float *xs, float *y, int m,
+                      int k, int n, void *stream);
+
 /* Text for a return code; never NULL, static storage. */
 const char *bqm_strerror(int rc);
 

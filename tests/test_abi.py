@@ -33,7 +33,7 @@ def test_header_declares_the_calls_and_strerror():
     assert declared_symbols() == sorted([
         "bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax", "bqm_e4m3_gemm",
         "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm", "bqm_q8_0_gemm_f8acc",
-        "bqm_strerror"])
+        "bqm_e4m3_nan_count", "bqm_e4m3_blk_quantize", "bqm_e4m3_blk_gemm", "bqm_strerror"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -160,6 +160,30 @@ def test_f16_mirror_validation(L):
     assert g(A16, B16, C16, 1, 96, 8, NUL) == 2             # k % 64
     assert g(A16, MIS2, C16, 1, 64, 8, NUL) == 2
     assert g(A16, B16, P(0x300002), 1, 64, 8, NUL) == 2
+
+
+def test_e4m3_blk_validation(L):
+    c = L.bqm_e4m3_nan_count
+    assert c(NUL, 16, B16, NUL) == 1
+    assert c(A16, 16, NUL, NUL) == 1
+    assert c(A16, 0, B16, NUL) == 1
+    assert c(MIS2, 16, B16, NUL) == 2
+    assert c(A16, 16, P(0x200004), NUL) == 2                # 8-byte counter alignment
+    q = L.bqm_e4m3_blk_quantize
+    assert q(NUL, B16, C16, 1, 128, NUL) == 1
+    assert q(A16, B16, C16, 0, 128, NUL) == 1
+    assert q(A16, B16, C16, 1, 64, NUL) == 1                 # k < 128
+    assert q(A16, B16, C16, 1, 192, NUL) == 2                # k % 128
+    assert q(P(0x100004), B16, C16, 1, 128, NUL) == 2        # x 16-byte alignment
+    assert q(A16, MIS2, C16, 1, 128, NUL) == 2
+    g = L.bqm_e4m3_blk_gemm
+    assert g(NUL, B16, C16, D16, A16, 1, 128, 8, NUL) == 1
+    assert g(A16, NUL, C16, D16, A16, 1, 128, 8, NUL) == 1
+    assert g(A16, B16, C16, D16, NUL, 1, 128, 8, NUL) == 1
+    assert g(A16, B16, C16, D16, A16, 1, 128, 0, NUL) == 1
+    assert g(A16, B16, C16, D16, A16, 1, 256 + 64, 8, NUL) == 2
+    assert g(MIS2, B16, C16, D16, A16, 1, 128, 8, NUL) == 2
+    assert g(A16, B16, P(0x300004), D16, A16, 1, 128, 8, NUL) == 2   # xq 16-byte alignment
 
 
 def test_product_path_never_touches_the_oracle():
