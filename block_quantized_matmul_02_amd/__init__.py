@@ -43,6 +43,7 @@ def lib() -> ctypes.CDLL:
         L.bqm_q8_0_gemv.argtypes = [P, I64, P, P, P, I, I, I, P]
         L.bqm_q8_0_gemm.argtypes = [P, I64, P, P, P, I, I, I, P]
         L.bqm_q8_0_gemm_f8acc.argtypes = [P, I64, P, P, P, I, I, I, P]
+        L.bqm_q8_0_gemv_f32.argtypes = [P, I64, P, P, I, I, I, P]
         L.bqm_e4m3_nan_count.argtypes = [P, I64, P, P]
         L.bqm_e4m3_blk_quantize.argtypes = [P, P, P, I, I, P]
         L.bqm_e4m3_blk_gemm.argtypes = [P, P, P, P, P, I, I, I, P]
@@ -54,7 +55,8 @@ def lib() -> ctypes.CDLL:
         L.bqm_f16_gemm.argtypes = [P, P, P, I, I, I, P]
         for fn in ("bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax",
                    "bqm_e4m3_gemm", "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm",
-                   "bqm_q8_0_gemm_f8acc", "bqm_e4m3_nan_count", "bqm_e4m3_blk_quantize", "bqm_e4m3_blk_gemm"):
+                   "bqm_q8_0_gemm_f8acc", "bqm_e4m3_nan_count", "bqm_e4m3_blk_quantize", "bqm_e4m3_blk_gemm",
+                   "bqm_q8_0_gemv_f32"):
             getattr(L, fn).restype = ctypes.c_int
         L.bqm_strerror.argtypes = [I]
         L.bqm_strerror.restype = ctypes.c_char_p
@@ -140,6 +142,22 @@ def bqm_q8_0_gemm(w, xq, xds, y=None):
     m, y = _q8_0_args(w, xq, xds, y, k, n)
     rc = lib().bqm_q8_0_gemm(_ptr(w), w.shape[1], _ptr(xq), _ptr(xds), _ptr(y), m, k, n, _stream(w))
     _raise("bqm_q8_0_gemm", rc)
+    return y
+
+
+def bqm_q8_0_gemv_f32(w, x, y=None):
+    """Decode step in one launch: q8_1 quantization of f32 ``x [m, k]`` and the Q8_0 GEMV against
+    ``w [n, row_bytes]`` -> f32 ``y [m, n]``, bitwise equal to bqm_q8_1_quantize + bqm_q8_0_gemv."""
+    import torch
+
+    n = w.shape[0]
+    m, k = x.shape
+    _check(w, torch.uint8, "w")
+    _check(x, torch.float32, "x")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _check(y, torch.float32, "y", (m, n))
+    _raise("bqm_q8_0_gemv_f32", lib().bqm_q8_0_gemv_f32(_ptr(w), w.shape[1], _ptr(x), _ptr(y), m, k, n, _stream(w)))
     return y
 
 

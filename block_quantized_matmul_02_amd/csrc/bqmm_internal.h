@@ -81,4 +81,43 @@ __device__ __forceinline__ float swap32_max(float v) {
     return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
+// The q8_1 rule for one 32-value block held by 8 consecutive lanes, four
+// values per lane: d = amax/127 (f32 division), q = clamp(round_half_away(
+// x/d), -127, 127) with a correctly rounded division, all zeros when d is 0.
+// Returns the lane's four quants packed little-endian into a dword and sets
+// d.  Every lane of the 8-lane group must execute it together (DPP).
+__device__ __forceinline__ float q8_1_max8(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+    return v;
+}
+
+__device__ __forceinline__ int q8_1_quant1(float x, float d, bool nz) {
+    if (!nz) return 0;
+    float r = __builtin_roundf(x / d);   // correctly rounded f32 division, ties away from zero
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+struct Q81Lane {
+    unsigned packed;   // quants 0..3 of this lane, byte i = quant i
+    int qsum;          // sum of this lane's four quants
+    float d;           // the block scale
+};
+
+__device__ __forceinline__ Q81Lane q8_1_block_lane(float4 v) {
+    const float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    const float amax = q8_1_max8(a);
+    const float d = amax / 127.0f;
+    const bool nz = d > 0.0f;   // amax == 0, or amax/127 underflowing to 0: an all-zero block
+    const int q0 = q8_1_quant1(v.x, d, nz), q1 = q8_1_quant1(v.y, d, nz);
+    const int q2 = q8_1_quant1(v.z, d, nz), q3 = q8_1_quant1(v.w, d, nz);
+    Q81Lane r;
+    r.packed = (unsigned)(q0 & 0xFF) | ((unsigned)(q1 & 0xFF) << 8) | ((unsigned)(q2 & 0xFF) << 16) | ((unsigned)q3 << 24);
+    r.qsum = q0 + q1 + q2 + q3;
+    r.d = d;
+    return r;
+}
+
 }  // namespace bqm

@@ -30,6 +30,12 @@
 //  * Every token's operation order is the same for any m, so an m-token call
 //    reproduces single-token calls bit for bit ("decode_kernel_census.rs"
 //    module doc: identical per-row FP order across decode and verify).
+//  * The QX variants take the f32 activation itself: every workgroup applies
+//    the q8_1 rule (the same device code as bqm_q8_1_quantize) to it while
+//    its first weight tiles are in flight and writes the quants and d_x
+//    straight into its LDS copy, so the quantize launch and the round trip
+//    of xq/xds through memory disappear from the decode step.  Results are
+//    bitwise those of bqm_q8_1_quantize followed by bqm_q8_0_gemv.
 #include "bqmm_internal.h"
 
 namespace bqm {
@@ -75,11 +81,25 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 // tiles are issued (PRE variants): up to 2 x 256 chunks of 16 bytes, m*k <= 8192.
 constexpr int kActPre = 2;
 
-// PRE = activation chunks per thread loaded ahead of the tiles (0 = none).
-template <int M, bool SINGLE, int PRE>
+// The four f32 values held in a 16-byte load.  The whole vector is bit cast:
+// clang lowers a bit cast of a vector-element expression to a read of the
+// vector's first element.
+__device__ __forceinline__ float4 as_float4(u32x4 b) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f f = __builtin_bit_cast(v4f, b);
+    return make_float4(f[0], f[1], f[2], f[3]);
+}
+
+// f32 activation float4s per thread a QX variant can hold in registers
+// (m*k <= 8192).
+constexpr int kActPreX = 8;
+
+// PRE = activation chunks per thread loaded ahead of the tiles (0 = none):
+// 16-byte chunks of xq, or with QX float4s of x.
+template <int M, bool SINGLE, int PRE, bool QX>
 __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     const uint8_t *__restrict__ w, int64_t w_row_bytes, const int8_t *__restrict__ xq,
-    const float *__restrict__ xds, float *__restrict__ y, int k, int n, GemvGeom g) {
+    const float *__restrict__ xds, const float *__restrict__ x, float *__restrict__ y, int k, int n, GemvGeom g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int nb = k / kQK;
     uint8_t *act_q = lds;                                  // [M][k] swizzled per pair
@@ -100,8 +120,9 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     // tile of the first wave of requests.  The PRE variants (m*k <= 8192,
     // m*k/32 <= 256) therefore issues its activation loads into registers
     // before the tiles' loads and waits for those alone.
-    const __amdgpu_buffer_rsrc_t rxq = make_rsrc(xq, (uint32_t)(M * k));
-    const __amdgpu_buffer_rsrc_t rxd = make_rsrc(xds, (uint32_t)(M * nb * 8));
+    const __amdgpu_buffer_rsrc_t rxq = make_rsrc(QX ? (const void *)x : (const void *)xq,
+                                                 (uint32_t)(QX ? M * k * 4 : M * k));
+    const __amdgpu_buffer_rsrc_t rxd = make_rsrc(xds, (uint32_t)(QX ? 0 : M * nb * 8));
     u32x4 pre_q[PRE > 0 ? PRE : 1];
     float pre_d;
     auto preload_activations = [&]() {
@@ -109,13 +130,36 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         for (int i = 0; i < PRE; i++)
             pre_q[i] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(rxq, (uint32_t)(threadIdx.x + kGemvThreads * i) * 16u, 0, 0));
-        pre_d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxd, threadIdx.x * 8u, 0, 0));
+        if (!QX) pre_d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxd, threadIdx.x * 8u, 0, 0));
+    };
+    // QX: float4 number c of x (values 4c..4c+3) quantized by its 8-lane
+    // group; its dword goes into the staged quants, and the group's first
+    // lane writes d_x.  Groups past the activation write into this wave's
+    // first tile, which is overwritten before it is read.
+    auto quantize_store = [&](float4 v, int c) {
+        const Q81Lane r = q8_1_block_lane(v);
+        const bool valid = c < M * k / 4;
+        const int t = (4 * c) / k;
+        const int e = 4 * c - t * k;                 // value index inside the token
+        const int cc = e >> 4, p = cc >> 2, ci = cc & 3;
+        uint8_t *dq = valid ? act_q + t * k + 64 * p + 16 * ((ci + (p >> 1)) & 3) + 4 * (c & 3) : tile0 + 4 * lane;
+        *reinterpret_cast<unsigned *>(dq) = r.packed;
+        float *dd = (valid && (c & 7) == 0) ? act_d + t * nb + (e >> 5) : reinterpret_cast<float *>(tile0) + lane;
+        *dd = r.d;
     };
     // Every preloaded value is stored unconditionally (values past the
     // activations go to this wave's first tile, which is overwritten before
     // it is read): a store behind a branch lets the compiler sink its load
     // into the branch, behind the tiles' loads.
     auto store_preloaded = [&]() {
+        if (QX) {
+#pragma unroll
+            for (int i = 0; i < PRE; i++) {
+                quantize_store(as_float4(pre_q[i]), (int)threadIdx.x + kGemvThreads * i);
+            }
+            __syncthreads();
+            return;
+        }
         const int chunks = M * k / 16;
 #pragma unroll
         for (int i = 0; i < PRE; i++) {
@@ -131,6 +175,17 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         __syncthreads();
     };
     auto stage_activations = [&]() {
+        if (QX) {
+            // every lane runs the same number of rounds, so each 8-lane group
+            // reduces with its full membership (loads past x return zeros)
+            const int rounds = (M * k / 4 + kGemvThreads - 1) / kGemvThreads;
+            for (int i = 0; i < rounds; i++) {
+                const int c = (int)threadIdx.x + kGemvThreads * i;
+                quantize_store(as_float4(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rxq, (uint32_t)c * 16u, 0, 0))), c);
+            }
+            __syncthreads();
+            return;
+        }
         const int chunks = M * k / 16;
         for (int c = threadIdx.x; c < chunks; c += kGemvThreads) {
             int t = c / (k / 16);
@@ -417,81 +472,92 @@ static bool make_geom(int k, int n, int64_t w_row_bytes, GemvGeom &g) {
     return true;
 }
 
-template <int M, bool SINGLE, int PRE>
-static int launch_variant(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y,
-                          int k, int n, const GemvGeom &g, int grid, int lds_bytes, hipStream_t stream) {
+template <int M, bool SINGLE, int PRE, bool QX>
+static int launch_variant(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
+                          float *y, int k, int n, const GemvGeom &g, int grid, int lds_bytes, hipStream_t stream) {
     static int attr_done = 0;
     if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, SINGLE, PRE>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, SINGLE, PRE, QX>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
         attr_done = 1;
     }
-    hipLaunchKernelGGL((q8_0_gemv_kernel<M, SINGLE, PRE>), dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w,
-                       w_row_bytes, xq, xds, y, k, n, g);
+    hipLaunchKernelGGL((q8_0_gemv_kernel<M, SINGLE, PRE, QX>), dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w,
+                       w_row_bytes, xq, xds, x, y, k, n, g);
     return launch_status();
 }
 
 // Resident workgroups per CU of the pipelined variant (registers and LDS),
 // at most 4.
-template <int M, int PRE>
+template <int M, int PRE, bool QX>
 static int gemv_per_cu(int lds_bytes) {
     static int attr_done = 0;   // allow up to 160 KiB of LDS before asking
     if (!attr_done) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE, QX>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
             return 1;
         attr_done = 1;
     }
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu,
+                                                     reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE, QX>),
                                                      kGemvThreads, lds_bytes) != hipSuccess || per_cu < 1)
         per_cu = 1;
     return per_cu > 4 ? 4 : per_cu;
 }
 
-template <int M>
-static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y,
-                       int k, int n, const GemvGeom &g, hipStream_t stream) {
-    const int nb = k / kQK;
-    const int act_bytes = (M * k + M * nb * 4 + 15) & ~15;
-    const int lds_bytes = act_bytes + kGemvWaves * 2 * g.TB;
+// Grid size and the pipelined / single-item choice, then the launch.
+template <int M, int PRE, bool QX>
+static int launch_sized(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
+                        float *y, int k, int n, const GemvGeom &g, int lds_bytes, hipStream_t stream) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    // the activations fit in the registers of the workgroup's threads
-    // (PRE variants are built for m <= 2, the decode sizes)
-    const int pre_chunks = (M * k / 16 + kGemvThreads - 1) / kGemvThreads;
-    const int pre = (M <= 2 && pre_chunks <= kActPre && M * nb <= kGemvThreads) ? pre_chunks : 0;
-    const int per_cu = pre == 1   ? gemv_per_cu<M, (M <= 2 ? 1 : 0)>(lds_bytes)
-                       : pre == 2 ? gemv_per_cu<M, (M <= 2 ? 2 : 0)>(lds_bytes)
-                                  : gemv_per_cu<M, 0>(lds_bytes);
+    const int per_cu = gemv_per_cu<M, PRE, QX>(lds_bytes);
     int want = (g.n_row_tiles + kGemvWaves - 1) / kGemvWaves;
     int grid = cus * per_cu;
     if (want < grid) grid = want;
     // every wave holds at most one item: the variant without the pipeline
     const bool single = (int64_t)g.n_row_tiles * g.nseg <= (int64_t)grid * kGemvWaves;
-    if (pre == 1) {
-        if (single) return launch_variant<M, true, (M <= 2 ? 1 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
-        return launch_variant<M, false, (M <= 2 ? 1 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
-    }
-    if (pre == 2) {
-        if (single) return launch_variant<M, true, (M <= 2 ? 2 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
-        return launch_variant<M, false, (M <= 2 ? 2 : 0)>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
-    }
-    if (single) return launch_variant<M, true, 0>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
-    return launch_variant<M, false, 0>(w, w_row_bytes, xq, xds, y, k, n, g, grid, lds_bytes, stream);
+    if (single) return launch_variant<M, true, PRE, QX>(w, w_row_bytes, xq, xds, x, y, k, n, g, grid, lds_bytes, stream);
+    return launch_variant<M, false, PRE, QX>(w, w_row_bytes, xq, xds, x, y, k, n, g, grid, lds_bytes, stream);
 }
 
-}  // namespace bqm
+template <int M>
+static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
+                       float *y, int k, int n, const GemvGeom &g, hipStream_t stream) {
+    const int nb = k / kQK;
+    const int act_bytes = (M * k + M * nb * 4 + 15) & ~15;
+    const int lds_bytes = act_bytes + kGemvWaves * 2 * g.TB;
+    if (x) {
+        // f32 activations: float4s per thread held in registers for m <= 2
+        // and m*k <= 8192 (rounded up to 1, 2, 4 or 8), else the staging loop
+        const int f4 = (M * k / 4 + kGemvThreads - 1) / kGemvThreads;
+        if (M <= 2 && f4 <= kActPreX) {
+            constexpr int P1 = M <= 2 ? 1 : 0, P2 = M <= 2 ? 2 : 0, P4 = M <= 2 ? 4 : 0, P8 = M <= 2 ? 8 : 0;
+            if (f4 <= 1) return launch_sized<M, P1, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+            if (f4 <= 2) return launch_sized<M, P2, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+            if (f4 <= 4) return launch_sized<M, P4, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+            return launch_sized<M, P8, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+        }
+        return launch_sized<M, 0, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+    }
+    // the activations fit in the registers of the workgroup's threads
+    // (PRE variants are built for m <= 2, the decode sizes)
+    const int pre_chunks = (M * k / 16 + kGemvThreads - 1) / kGemvThreads;
+    const int pre = (M <= 2 && pre_chunks <= kActPre && M * nb <= kGemvThreads) ? pre_chunks : 0;
+    if (pre == 1) return launch_sized<M, (M <= 2 ? 1 : 0), false>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+    if (pre == 2) return launch_sized<M, (M <= 2 ? 2 : 0), false>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+    return launch_sized<M, 0, false>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+}
 
-extern "C" int bqm_q8_0_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y,
-                             int m, int k, int n, void *stream) {
-    using namespace bqm;
-    if (!w || !xq || !xds || !y) return BQM_EINVAL;
+// Shared checks and the dispatch on m; x == nullptr selects the q8_1 inputs.
+static int gemv_entry(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
+                      float *y, int m, int k, int n, void *stream) {
     if (m < 1 || m > BQM_GEMV_MAX_M || k < 256 || n < 1) return BQM_EINVAL;
     if (k % 256 != 0) return BQM_EUNSUPPORTED;
     if (w_row_bytes < (int64_t)(k / kQK) * kQ80Bytes || w_row_bytes % 16 != 0) return BQM_EUNSUPPORTED;
-    if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xds, 8) || !aligned(y, 4)) return BQM_EUNSUPPORTED;
+    if (!aligned(w, 16) || !aligned(y, 4)) return BQM_EUNSUPPORTED;
+    if (x ? !aligned(x, 16) : (!aligned(xq, 16) || !aligned(xds, 8))) return BQM_EUNSUPPORTED;
     if ((int64_t)m * k * 9 / 8 > kActLdsMax) return BQM_EUNSUPPORTED;
     if (w_row_bytes > 0x7FFFFFFF / 64) return BQM_EUNSUPPORTED;
     GemvGeom g;
@@ -500,21 +566,35 @@ extern "C" int bqm_q8_0_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t
     if ((int64_t)g.RT * w_row_bytes > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
     hipStream_t s = as_stream(stream);
     switch (m) {
-        case 1: return launch_gemv<1>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 2: return launch_gemv<2>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 3: return launch_gemv<3>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 4: return launch_gemv<4>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 5: return launch_gemv<5>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 6: return launch_gemv<6>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 7: return launch_gemv<7>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 8: return launch_gemv<8>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 9: return launch_gemv<9>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 10: return launch_gemv<10>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 11: return launch_gemv<11>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 12: return launch_gemv<12>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 13: return launch_gemv<13>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 14: return launch_gemv<14>(w, w_row_bytes, xq, xds, y, k, n, g, s);
-        case 15: return launch_gemv<15>(w, w_row_bytes, xq, xds, y, k, n, g, s);
+        case 1: return launch_gemv<1>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 2: return launch_gemv<2>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 3: return launch_gemv<3>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 4: return launch_gemv<4>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 5: return launch_gemv<5>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 6: return launch_gemv<6>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 7: return launch_gemv<7>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 8: return launch_gemv<8>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 9: return launch_gemv<9>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 10: return launch_gemv<10>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 11: return launch_gemv<11>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 12: return launch_gemv<12>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 13: return launch_gemv<13>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 14: return launch_gemv<14>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
+        case 15: return launch_gemv<15>(w, w_row_bytes, xq, xds, x, y, k, n, g, s);
         default: return BQM_EINVAL;
     }
+}
+
+}  // namespace bqm
+
+extern "C" int bqm_q8_0_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y,
+                             int m, int k, int n, void *stream) {
+    if (!w || !xq || !xds || !y) return BQM_EINVAL;
+    return bqm::gemv_entry(w, w_row_bytes, xq, xds, nullptr, y, m, k, n, stream);
+}
+
+extern "C" int bqm_q8_0_gemv_f32(const uint8_t *w, int64_t w_row_bytes, const float *x, float *y, int m, int k, int n,
+                                 void *stream) {
+    if (!w || !x || !y) return BQM_EINVAL;
+    return bqm::gemv_entry(w, w_row_bytes, nullptr, nullptr, x, y, m, k, n, stream);
 }

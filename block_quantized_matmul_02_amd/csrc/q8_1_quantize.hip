@@ -16,25 +16,11 @@
 
 namespace bqm {
 
-__device__ __forceinline__ float max8(float v) {
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
-    return v;
-}
-
 __device__ __forceinline__ int isum8(int v) {
     v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
     v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
     v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
     return v;
-}
-
-__device__ __forceinline__ int quant1(float x, float d, bool nz) {
-    if (!nz) return 0;
-    float r = __builtin_roundf(x / d);   // correctly rounded f32 division, ties away from zero
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
 }
 
 // One thread per 4 values; blocks of 32 values = 8 consecutive lanes.
@@ -48,15 +34,11 @@ __global__ __launch_bounds__(256) void q8_1_quantize_kernel(const float4 *__rest
     // group is either entirely valid or entirely past the end.
     bool valid = i < nvec;
     float4 v = valid ? x[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    float amax = max8(a);
-    float d = amax / 127.0f;
-    bool nz = d > 0.0f;   // amax == 0, or amax/127 underflowing to 0: an all-zero block
-    int q0 = quant1(v.x, d, nz), q1 = quant1(v.y, d, nz), q2 = quant1(v.z, d, nz), q3 = quant1(v.w, d, nz);
-    int sum = isum8(q0 + q1 + q2 + q3);
+    const Q81Lane r = q8_1_block_lane(v);
+    int sum = isum8(r.qsum);
     if (valid) {
-        xq[i] = (q0 & 0xFF) | ((q1 & 0xFF) << 8) | ((q2 & 0xFF) << 16) | ((int)((unsigned)q3 << 24));
-        if ((threadIdx.x & 7) == 0) xds[i >> 3] = make_float2(d, d * (float)sum);
+        xq[i] = (int)r.packed;
+        if ((threadIdx.x & 7) == 0) xds[i >> 3] = make_float2(r.d, r.d * (float)sum);
     }
 }
 

@@ -93,6 +93,20 @@ int bqm_q8_0_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const
                   float *y, int m, int k, int n, void *stream);
 
 /*
+ * The decode step in one launch: bqm_q8_1_quantize of the f32 activation
+ * followed by bqm_q8_0_gemv, with the quantization done by every workgroup
+ * into its on-chip copy (same rule, same device code), so xq/xds never go
+ * through memory.  y is bitwise equal to the two-call path.
+ *   w, w_row_bytes, y, m, k, n : as bqm_q8_0_gemv (1 <= m <= 15, k % 256 == 0,
+ *                                the same on-chip limit m*k*9/8 <= 98304).
+ *   x : f32 activations [m][k], 16-byte aligned.
+ * ("decode_kernel_census.rs" fn q8: the q8_1 activation of the m=1 Q8_0
+ * GEMV; the pages run the quantizer as its own step.)
+ */
+int bqm_q8_0_gemv_f32(const uint8_t *w, int64_t w_row_bytes, const float *x, float *y, int m, int k, int n,
+                      void *stream);
+
+/*
  * Q8_0 prefill GEMM (MMQ), any m >= 1, built for m >= 16
  * ("accprobe_bench.rs" module doc: int8 MMA with an s32 accumulator per
  * k32 block folded every k32; "fp8_ffi.rs" module doc: the m>=16 arms).

@@ -33,7 +33,7 @@ def test_header_declares_the_calls_and_strerror():
     assert declared_symbols() == sorted([
         "bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax", "bqm_e4m3_gemm",
         "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm", "bqm_q8_0_gemm_f8acc",
-        "bqm_e4m3_nan_count", "bqm_e4m3_blk_quantize", "bqm_e4m3_blk_gemm", "bqm_strerror"])
+        "bqm_e4m3_nan_count", "bqm_e4m3_blk_quantize", "bqm_e4m3_blk_gemm", "bqm_q8_0_gemv_f32", "bqm_strerror"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -89,6 +89,23 @@ def test_q8_0_validation(L, fn):
     assert f(A16, rb, MIS2, C16, D16, 1, 4096, 8, NUL) == 2
     assert f(A16, rb, B16, P(0x300004), D16, 1, 4096, 8, NUL) == 2  # xds 8-byte alignment
     assert f(A16, rb, B16, C16, P(0x400002), 1, 4096, 8, NUL) == 2
+
+
+def test_gemv_f32_validation(L):
+    f = L.bqm_q8_0_gemv_f32
+    rb = 4096 // 32 * 34
+    assert f(NUL, rb, B16, D16, 1, 4096, 8, NUL) == 1
+    assert f(A16, rb, NUL, D16, 1, 4096, 8, NUL) == 1
+    assert f(A16, rb, B16, NUL, 1, 4096, 8, NUL) == 1
+    assert f(A16, rb, B16, D16, 0, 4096, 8, NUL) == 1
+    assert f(A16, rb, B16, D16, 16, 4096, 8, NUL) == 1             # m > 15
+    assert f(A16, rb, B16, D16, 1, 4096, 0, NUL) == 1
+    assert f(A16, rb, B16, D16, 1, 4096 + 32, 8, NUL) == 2         # k % 256
+    assert f(A16, rb - 16, B16, D16, 1, 4096, 8, NUL) == 2
+    assert f(A16, rb, P(0x100004), D16, 1, 4096, 8, NUL) == 2      # x 16-byte alignment
+    assert f(A16, rb, B16, P(0x400002), 1, 4096, 8, NUL) == 2
+    rb2 = 16384 // 32 * 34
+    assert f(A16, rb2, B16, D16, 9, 16384, 8, NUL) == 2            # on-chip limit
 
 
 def test_gemv_m_range_and_on_chip_limit(L):
