@@ -28,6 +28,15 @@ inline int launch_status() {
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Compute units of the current device (256 on MI355X, also the fallback).
+inline int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 256;
+    return cus;
+}
+
 // ---------------------------------------------------------------- device side
 
 // IEEE binary16 bits -> f32 (exact; hardware conversion handles subnormals).

@@ -342,8 +342,7 @@ extern "C" int bqm_e4m3_gemm(const uint8_t *w, const uint8_t *xq, const float *s
     if (k % 128 != 0) return BQM_EUNSUPPORTED;
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(scales, 4) || !aligned(y, 4)) return BQM_EUNSUPPORTED;
     if ((int64_t)kF8BM * k > 0x7FFFFFF0ll || (int64_t)320 * k > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int cus = device_cus();
     hipStream_t s = as_stream(stream);
     switch (pick_nt(m, n, cus)) {
         case 2: return launch_f8<2>(w, xq, scales, y, m, k, n, s);

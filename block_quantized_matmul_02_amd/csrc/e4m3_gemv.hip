@@ -234,8 +234,7 @@ static int e8_launch(const uint8_t *w, const float *x, float w_scale, float *y, 
         if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
         attr_done = 1;
     }
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int cus = device_cus();
     // resident workgroups per CU (registers and LDS), at most 4
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&e4m3_gemv_kernel<TG, JM, XREG>),

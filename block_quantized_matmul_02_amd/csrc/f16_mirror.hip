@@ -273,8 +273,7 @@ extern "C" int bqm_f16_gemm(const uint16_t *w16, const uint16_t *x16, float *y, 
     if (k % 64 != 0) return BQM_EUNSUPPORTED;
     if (!aligned(w16, 16) || !aligned(x16, 16) || !aligned(y, 4)) return BQM_EUNSUPPORTED;
     if ((int64_t)kH16BM * 2 * k > 0x7FFFFFF0ll || (int64_t)320 * 2 * k > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int cus = device_cus();
     hipStream_t s = as_stream(stream);
     switch (h16_pick_nt(m, n, cus)) {
         case 2: return launch_h16<2>(w16, x16, y, m, k, n, s);
