@@ -18,14 +18,22 @@
 //    operands are read two blocks ahead, so the matrix core, the LDS and the
 //    VALU overlap.  MFMA results stay in ordinary VGPRs (the build asks for
 //    the VGPR form), so the fold reads them without copies.
-//  * Workgroup tile 64 tokens x 64 weight rows, 4 waves of 32x32; k is staged
-//    256 values (8 blocks) at a time into double-buffered LDS, and the global
-//    loads run two stages ahead in a register double buffer to cover L2 and
-//    Infinity Cache latency (one barrier per stage).
-//  * Weight rows are 34-byte blocks whose quants are 2-byte aligned.  Each
-//    thread loads one 68-byte block pair (4-byte aligned) straight into
-//    registers, realigns the even block with v_alignbit, and writes dense
-//    quants plus f32 scales to LDS.
+//  * Workgroup tile BM tokens x 64 weight rows, BM/16 waves of 32x32; k is
+//    staged 256 values (8 blocks) at a time into double-buffered LDS, and the
+//    global loads run two stages ahead in a register double buffer to cover
+//    L2 and Infinity Cache latency (one barrier per stage).  BM = 128 (8
+//    waves, one workgroup per CU) loads a quarter less per output than BM =
+//    64 (4 waves, two workgroups per CU): per output a workgroup reads 1/64
+//    of a weight row plus 1/BM of an activation row, and the vector memory
+//    pipeline, not the matrix cores, is what the loads contend for.  The
+//    taller tile is used when its workgroups fill whole rounds of the CUs
+//    (measured: 10% faster at m=512, N=4096 and 20480, but slower wherever a
+//    partial last round or fewer tiles than CUs remain).
+//  * Weight rows are 34-byte blocks whose quants are 2-byte aligned.  A
+//    68-byte block pair (4-byte aligned) is loaded by two threads straight
+//    into registers: one takes dwords 0..8 and realigns the even block with
+//    v_alignbit, the other dwords 8..16 (the odd block, already aligned);
+//    each writes dense quants plus its f32 scale to LDS.
 //  * Quant tiles are stored with a padded row stride of 272 bytes (256 + 16),
 //    so the MFMA operand reads of 8 consecutive rows at the same k hit
 //    distinct banks and every LDS address is a per-lane base plus a
@@ -48,12 +56,10 @@
 
 namespace bqm {
 
-constexpr int kMmqBM = 64;
 constexpr int kMmqBN = 64;
 constexpr int kMmqKB = 256;                  // k values per stage = 8 blocks
 constexpr int kMmqBlocks = kMmqKB / kQK;     // 8
 constexpr int kMmqPairBytes = 2 * kQ80Bytes; // 68
-constexpr int kMmqThreads = 256;
 constexpr int kMmqRowStride = kMmqKB + 16;   // 272: padded LDS row of quants
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t mmq_rsrc(const void *base, int64_t bytes) {
@@ -61,30 +67,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mmq_rsrc(const void *base, int
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)b, 0x00020000);
 }
 
+template <int BM>
 struct MmqStage {
-    uint8_t x[kMmqBM * kMmqRowStride];   // activation quants, padded rows
+    uint8_t x[BM * kMmqRowStride];       // activation quants, padded rows
     uint8_t w[kMmqBN * kMmqRowStride];   // weight quants, padded rows
     // d_x / d_w per block and row; rows padded by 8 floats so that the
     // stores (8 blocks of a row from neighbouring threads) hit distinct banks
-    float dx[kMmqBlocks][kMmqBM + 8];
+    float dx[kMmqBlocks][BM + 8];
     float dw[kMmqBlocks][kMmqBN + 8];
 };
-static_assert(2 * sizeof(MmqStage) * 2 <= 160 * 1024, "two workgroups per CU");
+static_assert(2 * sizeof(MmqStage<128>) <= 160 * 1024, "one 128-row workgroup per CU");
+static_assert(4 * sizeof(MmqStage<64>) <= 160 * 1024, "two 64-row workgroups per CU");
 
-// Global loads of one stage, held in registers until written to LDS.
+// Global loads of one stage, held in registers until written to LDS.  The
+// 256 block pairs of a stage's weight tile are loaded as 512 halves, WH per
+// thread.
+template <int WH>
 struct MmqRegs {
-    u32x4 x[4];      // 4 activation chunks
-    u32x4 w[4];      // one 68-byte weight block pair: dwords 0..15
-    uint32_t w16;    // and dword 16
-    float dx[2];     // 2 (row, block) activation scales
+    u32x4 x[4];         // 4 activation chunks
+    u32x4 w[WH][2];     // half a 68-byte weight block pair: dwords 0..7, or 9..16
+    uint32_t w8[WH];    // and dword 8 (the odd block's scale sits in its high half)
+    float dx[2];        // 2 (row, block) activation scales
 };
 
-template <bool F8ACC>
-__global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *__restrict__ w, int64_t w_row_bytes,
+template <int BM, bool F8ACC>
+__global__ __launch_bounds__(4 * BM) void q8_0_gemm_kernel(const uint8_t *__restrict__ w, int64_t w_row_bytes,
                                                               const int8_t *__restrict__ xq,
                                                               const float *__restrict__ xds, float *__restrict__ y,
                                                               int m, int k, int n) {
-    __shared__ __attribute__((aligned(16))) MmqStage st[2];
+    constexpr int kMmqThreads = 4 * BM;
+    constexpr int WH = 512 / kMmqThreads;   // weight half-pairs per thread
+    using Stage = MmqStage<BM>;
+    using Regs = MmqRegs<WH>;
+    __shared__ __attribute__((aligned(16))) Stage st[2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -94,13 +109,13 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
     // (id % 8), and each XCD has its own L2.  Renumber so that XCD x runs a
     // contiguous range of tiles, m-tile fastest: the token tiles that share a
     // weight tile then run together on one XCD and read it once into its L2.
-    const int nm = (m + kMmqBM - 1) / kMmqBM;
+    const int nm = (m + BM - 1) / BM;
     const int ntiles = gridDim.x;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int per = ntiles >> 3, extra = ntiles & 7;
     const int tile = xcd * per + min(xcd, extra) + slot;
     const int n0 = (tile / nm) * kMmqBN;
-    const int m0 = (tile - (tile / nm) * nm) * kMmqBM;
+    const int m0 = (tile - (tile / nm) * nm) * BM;
     const int nb = k / kQK;
     const int nstage = k / kMmqKB;
 
@@ -111,73 +126,82 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
 
     // This thread's load slots, as byte offsets fixed for the whole kernel; the
     // stage offset is a uniform scalar added by the buffer load (soffset).
-    // X: 4 chunks (row q>>4, chunk q&15).  W: one 68-byte block pair (row
-    // tid>>2, pair tid&3).  dX: 2 (row q>>3, block q&7), the d of each pair.
-    const int wrow = tid >> 2, wpair = tid & 3;
-    const uint32_t woff = (uint32_t)(wrow * w_row_bytes + kMmqPairBytes * wpair);
+    // X: 4 chunks (row q>>4, chunk q&15).  W: half-pairs h = tid + 4*BM*j,
+    // half h of pair p = h%256 (row p>>2, pair p&3): h < 256 the even block,
+    // else the odd one.  dX: 2 (row q>>3, block q&7), the d of each pair.
+    int wrow[WH], wpair[WH], odd[WH];
+    uint32_t wo0[WH], wo1[WH], wo2[WH];
+#pragma unroll
+    for (int j = 0; j < WH; j++) {
+        const int h = tid + kMmqThreads * j;
+        const int wp = h & 255;
+        odd[j] = h >> 8;                     // the same for a whole wave
+        wrow[j] = wp >> 2;
+        wpair[j] = wp & 3;
+        const uint32_t wbase = (uint32_t)(wrow[j] * w_row_bytes + kMmqPairBytes * wpair[j]);
+        // even: b128 at +0 and +16 (dwords 0..7), b32 at +32 (dword 8)
+        // odd:  b128 at +36 and +52 (dwords 9..16), b32 at +32 (dword 8)
+        wo0[j] = wbase + (odd[j] ? 36u : 0u);
+        wo1[j] = wbase + (odd[j] ? 52u : 16u);
+        wo2[j] = wbase + 32u;
+    }
     uint32_t xoff[4], doff[2];
 #pragma unroll
     for (int s = 0; s < 4; s++) {
-        const int q = tid + 256 * s;
+        const int q = tid + kMmqThreads * s;
         xoff[s] = (uint32_t)((q >> 4) * k + 16 * (q & 15));
     }
 #pragma unroll
     for (int s = 0; s < 2; s++) {
-        const int q = tid + 256 * s;
+        const int q = tid + kMmqThreads * s;
         doff[s] = (uint32_t)(((q >> 3) * nb + (q & 7)) * 8);
     }
-    auto load_stage = [&](MmqRegs &R, int kc) {
+    auto load_stage = [&](Regs &R, int kc) {
         const int sx = kc * kMmqKB, sw = kc * (kMmqBlocks * kQ80Bytes), sd = kc * kMmqBlocks * 8;
 #pragma unroll
         for (int s = 0; s < 4; s++)
             R.x[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rX, xoff[s], sx, 0));
 #pragma unroll
-        for (int s = 0; s < 4; s++)
-            R.w[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, woff + 16 * s, sw, 0));
-        R.w16 = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, woff + 64, sw, 0);
+        for (int j = 0; j < WH; j++) {
+            R.w[j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, wo0[j], sw, 0));
+            R.w[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, wo1[j], sw, 0));
+            R.w8[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, wo2[j], sw, 0);
+        }
 #pragma unroll
         for (int s = 0; s < 2; s++)
             R.dx[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, doff[s], sd, 0));
     };
-    auto store_stage = [&](MmqStage &S, const MmqRegs &R) {
+    auto store_stage = [&](Stage &S, const Regs &R) {
 #pragma unroll
         for (int s = 0; s < 4; s++) {
-            int q = tid + 256 * s;
+            int q = tid + kMmqThreads * s;
             int row = q >> 4, c = q & 15;
             *reinterpret_cast<u32x4 *>(S.x + row * kMmqRowStride + 16 * c) = R.x[s];
         }
-        // realign the block pair: the even block's quants start 2 bytes into dword 0
-        uint32_t d[17];
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-            d[4 * s + 0] = R.w[s][0];
-            d[4 * s + 1] = R.w[s][1];
-            d[4 * s + 2] = R.w[s][2];
-            d[4 * s + 3] = R.w[s][3];
+        for (int j = 0; j < WH; j++) {
+            // the even block's quants start 2 bytes into dword 0: realign them
+            // (an odd half's realigned words are computed too and not used)
+            const uint32_t d[9] = {R.w[j][0][0], R.w[j][0][1], R.w[j][0][2], R.w[j][0][3],
+                                   R.w[j][1][0], R.w[j][1][1], R.w[j][1][2], R.w[j][1][3], R.w8[j]};
+            u32x4 qa0, qa1;
+            qa0[0] = __builtin_amdgcn_alignbit(d[1], d[0], 16u);
+            qa0[1] = __builtin_amdgcn_alignbit(d[2], d[1], 16u);
+            qa0[2] = __builtin_amdgcn_alignbit(d[3], d[2], 16u);
+            qa0[3] = __builtin_amdgcn_alignbit(d[4], d[3], 16u);
+            qa1[0] = __builtin_amdgcn_alignbit(d[5], d[4], 16u);
+            qa1[1] = __builtin_amdgcn_alignbit(d[6], d[5], 16u);
+            qa1[2] = __builtin_amdgcn_alignbit(d[7], d[6], 16u);
+            qa1[3] = __builtin_amdgcn_alignbit(d[8], d[7], 16u);
+            const int b = 2 * wpair[j] + odd[j];
+            uint8_t *wr = S.w + wrow[j] * kMmqRowStride + 32 * b;
+            *reinterpret_cast<u32x4 *>(wr + 0) = odd[j] ? R.w[j][0] : qa0;
+            *reinterpret_cast<u32x4 *>(wr + 16) = odd[j] ? R.w[j][1] : qa1;
+            S.dw[b][wrow[j]] = half_bits_to_float(odd[j] ? (R.w8[j] >> 16) : (d[0] & 0xFFFFu));
         }
-        d[16] = R.w16;
-        u32x4 qa0, qa1;
-        qa0[0] = __builtin_amdgcn_alignbit(d[1], d[0], 16u);
-        qa0[1] = __builtin_amdgcn_alignbit(d[2], d[1], 16u);
-        qa0[2] = __builtin_amdgcn_alignbit(d[3], d[2], 16u);
-        qa0[3] = __builtin_amdgcn_alignbit(d[4], d[3], 16u);
-        qa1[0] = __builtin_amdgcn_alignbit(d[5], d[4], 16u);
-        qa1[1] = __builtin_amdgcn_alignbit(d[6], d[5], 16u);
-        qa1[2] = __builtin_amdgcn_alignbit(d[7], d[6], 16u);
-        qa1[3] = __builtin_amdgcn_alignbit(d[8], d[7], 16u);
-        const u32x4 qb0 = {d[9], d[10], d[11], d[12]};
-        const u32x4 qb1 = {d[13], d[14], d[15], d[16]};
-        const int b0 = 2 * wpair;
-        uint8_t *wr = S.w + wrow * kMmqRowStride + 32 * b0;
-        *reinterpret_cast<u32x4 *>(wr + 0) = qa0;
-        *reinterpret_cast<u32x4 *>(wr + 16) = qa1;
-        *reinterpret_cast<u32x4 *>(wr + 32) = qb0;
-        *reinterpret_cast<u32x4 *>(wr + 48) = qb1;
-        S.dw[b0][wrow] = half_bits_to_float(d[0]);
-        S.dw[b0 + 1][wrow] = half_bits_to_float(d[8] >> 16);
 #pragma unroll
         for (int s = 0; s < 2; s++) {
-            int q = tid + 256 * s;
+            int q = tid + kMmqThreads * s;
             S.dx[q & 7][q >> 3] = R.dx[s];
         }
     };
@@ -199,7 +223,7 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
     // in the same register layout as the int32 block sums.  That leaves two
     // VALU ops per output and block: convert S, then fma into the
     // accumulator.  The outer products of a pair are issued one pair ahead.
-    auto compute_stage = [&](const MmqStage &S) {
+    auto compute_stage = [&](const Stage &S) {
         v4i A[3], B[3];
         const uint8_t *xa = S.x + arow * kMmqRowStride + 16 * khalf;
         const uint8_t *wb = S.w + brow * kMmqRowStride + 16 * khalf;
@@ -224,13 +248,11 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
         using BlockSum = typename std::conditional<F8ACC, v16f, v16i>::type;
         auto block_sum = [&](const v4i &a, const v4i &b) -> BlockSum {
             if constexpr (F8ACC) {
+                typedef long v2l __attribute__((ext_vector_type(2)));
                 const v16f zf = {0};
-                const long alo = ((long)(uint32_t)a[1] << 32) | (uint32_t)a[0];
-                const long ahi = ((long)(uint32_t)a[3] << 32) | (uint32_t)a[2];
-                const long blo = ((long)(uint32_t)b[1] << 32) | (uint32_t)b[0];
-                const long bhi = ((long)(uint32_t)b[3] << 32) | (uint32_t)b[2];
-                const v16f lo = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(alo, blo, zf, 0, 0, 0);
-                return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(ahi, bhi, lo, 0, 0, 0);
+                const v2l av = __builtin_bit_cast(v2l, a), bv = __builtin_bit_cast(v2l, b);
+                const v16f lo = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av[0], bv[0], zf, 0, 0, 0);
+                return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av[1], bv[1], lo, 0, 0, 0);
             } else {
                 const v16i z = {0};
                 return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
@@ -273,7 +295,7 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
     // hit): with a branch around them the compiler cannot count the loads in
     // flight, and its wait before writing the older register buffer to LDS
     // would then also wait for the loads just issued.
-    MmqRegs R0, R1;
+    Regs R0, R1;
     const int last = nstage - 1;
     load_stage(R0, 0);
     load_stage(R1, min(1, last));
@@ -304,7 +326,18 @@ __global__ __launch_bounds__(kMmqThreads) void q8_0_gemm_kernel(const uint8_t *_
     }
 }
 
-// Checks shared by both arms, then the launch.
+template <int BM, bool F8ACC>
+static int launch_tiles(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y, int m,
+                        int k, int n, int64_t tiles, hipStream_t s) {
+    if (tiles > 0x7FFFFFFF) return BQM_EUNSUPPORTED;
+    hipLaunchKernelGGL((q8_0_gemm_kernel<BM, F8ACC>), dim3((unsigned)tiles), dim3(4 * BM), 0, s, w, w_row_bytes, xq,
+                       xds, y, m, k, n);
+    return launch_status();
+}
+
+// Checks shared by both arms, the tile height, then the launch.  The
+// 128-row tile runs one workgroup per CU, so it is taken only when its
+// workgroups fill whole rounds of the CUs, the last round at least 3/4 full.
 template <bool F8ACC>
 static int launch_mmq(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y, int m,
                       int k, int n, void *stream) {
@@ -313,14 +346,16 @@ static int launch_mmq(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, c
     if (k % 256 != 0) return BQM_EUNSUPPORTED;
     if (w_row_bytes < (int64_t)(k / kQK) * kQ80Bytes || w_row_bytes % 16 != 0) return BQM_EUNSUPPORTED;
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xds, 8) || !aligned(y, 4)) return BQM_EUNSUPPORTED;
-    // per-workgroup offsets are 32-bit: 64 rows of activations / weights
-    if ((int64_t)kMmqBM * k > 0x7FFFFFF0ll || (int64_t)kMmqBN * w_row_bytes > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
-    const int64_t tiles = (int64_t)((n + kMmqBN - 1) / kMmqBN) * ((m + kMmqBM - 1) / kMmqBM);
-    if (tiles > 0x7FFFFFFF) return BQM_EUNSUPPORTED;
-    dim3 grid((unsigned)tiles);
-    hipLaunchKernelGGL(q8_0_gemm_kernel<F8ACC>, grid, dim3(kMmqThreads), 0, as_stream(stream), w, w_row_bytes, xq,
-                       xds, y, m, k, n);
-    return launch_status();
+    // per-workgroup offsets are 32-bit: 128 rows of activations, 64 of weights
+    if ((int64_t)128 * k > 0x7FFFFFF0ll || (int64_t)kMmqBN * w_row_bytes > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
+    const int64_t ntiles = (n + kMmqBN - 1) / kMmqBN;
+    const int64_t tall = ntiles * ((m + 127) / 128);
+    const int64_t cus = device_cus();
+    const int64_t last = tall % cus;
+    hipStream_t s = as_stream(stream);
+    if (tall >= cus && (last == 0 || 4 * last >= 3 * cus))
+        return launch_tiles<128, F8ACC>(w, w_row_bytes, xq, xds, y, m, k, n, tall, s);
+    return launch_tiles<64, F8ACC>(w, w_row_bytes, xq, xds, y, m, k, n, ntiles * ((m + 63) / 64), s);
 }
 
 }  // namespace bqm
