@@ -112,7 +112,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["gemv", "mmq", "e4m3", "e4m3_gemv", "f16", "accprobe", "e4m3_blk", "copy"], default=None,
                     help="run one part only (for profiler passes); 'copy' runs a plain 1 GiB device copy "
