@@ -114,7 +114,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["gemv", "mmq", "e4m3", "e4m3_gemv", "f16", "accprobe", "e4m3_blk", "copy"], default=None,
+    ap.add_argument("--only", choices=["gemv", "sweep", "mmq", "e4m3", "e4m3_gemv", "f16", "accprobe", "e4m3_blk", "copy"], default=None,
                     help="run one part only (for profiler passes); 'copy' runs a plain 1 GiB device copy "
                          "that calibrates the HBM byte counters")
     args = ap.parse_args()
@@ -192,6 +192,42 @@ def main():
         })
         del ws
         torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- decode / verify sweep
+    if args.only in (None, "sweep"):
+        sweep = {}
+        for k, n in workloads.GEMV_SWEEP_SHAPES:
+            w0 = torch.from_numpy(workloads.q8_0_weights(n, k, rng)).to(dev)
+            copies = max(3, -(-600_000_000 // w0.numel()))        # rotate >= 600 MB past the 256 MB cache
+            ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+            for m in (1, 9):
+                log(f"[bench] sweep m={m} {k}->{n}")
+                x = torch.from_numpy(workloads.activations(m, k, rng)).to(dev)
+                y = torch.empty((m, n), dtype=torch.float32, device=dev)
+                xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+                xds = torch.empty((m, k // 32, 2), dtype=torch.float32, device=dev)
+                byts = n * (k // 32) * 34 + m * k * 4 + m * n * 4
+                row = {}
+                if m <= 2 and m * k <= 8192:          # the one-launch step is for decode
+                    fns = [("gemv_f32", lambda s: bqm.bqm_q8_0_gemv_f32(ws[s % copies], x, y))]
+                    timed_loop(torch, stream, args.warmup, fns)
+                    _, per = timed_loop(torch, stream, args.steps, fns)
+                    row["one_launch_us"] = round(per["gemv_f32"] * 1e3, 2)
+                fns2 = [("quantize", lambda s: bqm.bqm_q8_1_quantize(x, xq, xds)),
+                        ("gemv", lambda s: bqm.bqm_q8_0_gemv(ws[s % copies], xq, xds, y))]
+                timed_loop(torch, stream, args.warmup, fns2)
+                t2, per2 = timed_loop(torch, stream, args.steps, fns2)
+                row["two_launch_step_us"] = round(t2 / args.steps * 1e3, 2)
+                row["two_launch_gemv_us"] = round(per2["gemv"] * 1e3, 2)
+                best = min(row.get("one_launch_us", 1e9), row["two_launch_step_us"])
+                gbs = byts / (best * 1e-6) / 1e9
+                row.update({"step_us": best, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+                sweep[f"m{m} {k}->{n}"] = row
+            del ws, w0
+        torch.cuda.empty_cache()
+        out["gemv_sweep"] = {"workload": "decode/verify sweep: q8_1 quantize + Q8_0 GEMV per step (the faster of "
+                                         "the one-launch and two-launch paths), weights rotated past the cache",
+                             **sweep}
 
     # ---------------------------------------------------------------- prefill MMQ
     if args.only in (None, "mmq"):

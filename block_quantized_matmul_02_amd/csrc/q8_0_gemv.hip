@@ -96,10 +96,21 @@ constexpr int kActPreX = 8;
 
 // PRE = activation chunks per thread loaded ahead of the tiles (0 = none):
 // 16-byte chunks of xq, or with QX float4s of x.
-template <int M, bool SINGLE, int PRE, bool QX>
+// Most tokens whose activation operands a lane holds in registers (XR).
+// Measured on the sweep shapes: holding them for 3..9 tokens costs more in
+// occupancy (178..320 VGPRs) than it saves in LDS reads (m=9, 4096 -> 20480:
+// 40.5 us against 36.5 us).
+constexpr int kXregMaxM = 2;
+
+// XR: every row gives a lane the same pairs (whole rows, one pair per lane:
+// K <= 4096), so the lane's activation operands for all M tokens are loaded
+// from LDS once and held in registers.
+template <int M, bool SINGLE, int PRE, bool QX, bool XR>
 __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     const uint8_t *__restrict__ w, int64_t w_row_bytes, const int8_t *__restrict__ xq,
     const float *__restrict__ xds, const float *__restrict__ x, float *__restrict__ y, int k, int n, GemvGeom g) {
+    static_assert(!QX || PRE > 0, "f32 activations are held in registers");
+    static_assert(!XR || M <= kXregMaxM, "register-held activations for at most kXregMaxM tokens");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int nb = k / kQK;
     uint8_t *act_q = lds;                                  // [M][k] swizzled per pair
@@ -175,17 +186,6 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         __syncthreads();
     };
     auto stage_activations = [&]() {
-        if (QX) {
-            // every lane runs the same number of rounds, so each 8-lane group
-            // reduces with its full membership (loads past x return zeros)
-            const int rounds = (M * k / 4 + kGemvThreads - 1) / kGemvThreads;
-            for (int i = 0; i < rounds; i++) {
-                const int c = (int)threadIdx.x + kGemvThreads * i;
-                quantize_store(as_float4(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rxq, (uint32_t)c * 16u, 0, 0))), c);
-            }
-            __syncthreads();
-            return;
-        }
         const int chunks = M * k / 16;
         for (int c = threadIdx.x; c < chunks; c += kGemvThreads) {
             int t = c / (k / 16);
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     // Register copy of this lane's activation pair, filled once the
     // activations are staged (used when every row gives the lane the same
     // pair; see compute).
-    ActPair xreg[M <= 2 ? M : 1];
+    ActPair xreg[XR ? M : 1];
 
     // One pair (two blocks) of tile row rl, pair pl of the segment, for every
     // token: a[t] += d_w*d_x*S for both blocks.  The activation operands come
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
                 for (int t = 0; t < M; t++) a0[t] = 0.0f;
                 for (int j = 0; j < g.J; j++) {
                     const int pl = li + g.L * j;
-                    if (pl < g.PS) pair_dot(tl, rl, pl, 0, a0, nullptr);
+                    if (pl < g.PS) pair_dot(tl, rl, pl, 0, a0, XR ? xreg : nullptr);
                 }
                 reduce_store(a0, row0 + rl);
             }
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     // and m <= 2: the activation operands sit in registers, and the two tiles
     // run as two independent chains so the LDS and dot-product latencies of
     // one overlap the other's.
-    const bool fast = M <= 2 && g.nseg == 1 && g.J == 1;
+    constexpr bool fast = XR && M <= 2;
     auto compute_pair_fast = [&](int q, const uint8_t *t0, const uint8_t *t1, bool two) {
         const int row0 = (wid + nwaves * q) * g.RT;
         const int row1 = (wid + nwaves * (q + 1)) * g.RT;
@@ -379,9 +379,9 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     };
 
     auto load_xreg = [&]() {
-        if (fast && li < g.PS) {
+        if (XR && li < g.PS) {
 #pragma unroll
-            for (int t = 0; t < (M <= 2 ? M : 1); t++) xreg[t] = load_act(t, li);
+            for (int t = 0; t < (XR ? M : 1); t++) xreg[t] = load_act(t, li);
         }
     };
 
@@ -472,46 +472,46 @@ static bool make_geom(int k, int n, int64_t w_row_bytes, GemvGeom &g) {
     return true;
 }
 
-template <int M, bool SINGLE, int PRE, bool QX>
+template <int M, bool SINGLE, int PRE, bool QX, bool XR>
 static int launch_variant(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
                           float *y, int k, int n, const GemvGeom &g, int grid, int lds_bytes, hipStream_t stream) {
     static int attr_done = 0;
     if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, SINGLE, PRE, QX>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, SINGLE, PRE, QX, XR>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
         attr_done = 1;
     }
-    hipLaunchKernelGGL((q8_0_gemv_kernel<M, SINGLE, PRE, QX>), dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w,
+    hipLaunchKernelGGL((q8_0_gemv_kernel<M, SINGLE, PRE, QX, XR>), dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w,
                        w_row_bytes, xq, xds, x, y, k, n, g);
     return launch_status();
 }
 
 // Resident workgroups per CU of the pipelined variant (registers and LDS),
 // at most 4.
-template <int M, int PRE, bool QX>
+template <int M, int PRE, bool QX, bool XR>
 static int gemv_per_cu(int lds_bytes) {
     static int attr_done = 0;   // allow up to 160 KiB of LDS before asking
     if (!attr_done) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE, QX>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE, QX, XR>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
             return 1;
         attr_done = 1;
     }
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu,
-                                                     reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE, QX>),
+                                                     reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE, QX, XR>),
                                                      kGemvThreads, lds_bytes) != hipSuccess || per_cu < 1)
         per_cu = 1;
     return per_cu > 4 ? 4 : per_cu;
 }
 
 // Grid size and the pipelined / single-item choice, then the launch.
-template <int M, int PRE, bool QX>
+template <int M, int PRE, bool QX, bool XR>
 static int launch_sized(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
                         float *y, int k, int n, const GemvGeom &g, int lds_bytes, hipStream_t stream) {
     const int cus = device_cus();
-    const int per_cu = gemv_per_cu<M, PRE, QX>(lds_bytes);
+    const int per_cu = gemv_per_cu<M, PRE, QX, XR>(lds_bytes);
     int want = (g.n_row_tiles + kGemvWaves - 1) / kGemvWaves;
     int grid = cus * per_cu;
     if (want < grid) grid = want;
@@ -522,8 +522,19 @@ static int launch_sized(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq,
     grid = (int)(((int64_t)g.n_row_tiles + tpw * kGemvWaves - 1) / (tpw * kGemvWaves));
     // every wave holds at most one item: the variant without the pipeline
     const bool single = (int64_t)g.n_row_tiles * g.nseg <= (int64_t)grid * kGemvWaves;
-    if (single) return launch_variant<M, true, PRE, QX>(w, w_row_bytes, xq, xds, x, y, k, n, g, grid, lds_bytes, stream);
-    return launch_variant<M, false, PRE, QX>(w, w_row_bytes, xq, xds, x, y, k, n, g, grid, lds_bytes, stream);
+    if (single)
+        return launch_variant<M, true, PRE, QX, XR>(w, w_row_bytes, xq, xds, x, y, k, n, g, grid, lds_bytes, stream);
+    return launch_variant<M, false, PRE, QX, XR>(w, w_row_bytes, xq, xds, x, y, k, n, g, grid, lds_bytes, stream);
+}
+
+template <int M, int PRE, bool QX>
+static int launch_xr(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
+                     float *y, int k, int n, const GemvGeom &g, int lds_bytes, hipStream_t stream) {
+    if constexpr (M <= kXregMaxM) {
+        if (g.nseg == 1 && g.J == 1)
+            return launch_sized<M, PRE, QX, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+    }
+    return launch_sized<M, PRE, QX, false>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
 }
 
 template <int M>
@@ -532,26 +543,24 @@ static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, 
     const int nb = k / kQK;
     const int act_bytes = (M * k + M * nb * 4 + 15) & ~15;
     const int lds_bytes = act_bytes + kGemvWaves * 2 * g.TB;
-    if (x) {
-        // f32 activations: float4s per thread held in registers for m <= 2
-        // and m*k <= 8192 (rounded up to 1, 2, 4 or 8), else the staging loop
-        const int f4 = (M * k / 4 + kGemvThreads - 1) / kGemvThreads;
-        if (M <= 2 && f4 <= kActPreX) {
-            constexpr int P1 = M <= 2 ? 1 : 0, P2 = M <= 2 ? 2 : 0, P4 = M <= 2 ? 4 : 0, P8 = M <= 2 ? 8 : 0;
-            if (f4 <= 1) return launch_sized<M, P1, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
-            if (f4 <= 2) return launch_sized<M, P2, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
-            if (f4 <= 4) return launch_sized<M, P4, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
-            return launch_sized<M, P8, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+    if constexpr (M <= 2) {
+        if (x) {
+            // f32 activations held in registers, 1, 2, 4 or 8 float4s per
+            // thread (the entry point admits m <= 2, m*k <= 8192)
+            const int f4 = (M * k / 4 + kGemvThreads - 1) / kGemvThreads;
+            if (f4 <= 1) return launch_xr<M, 1, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+            if (f4 <= 2) return launch_xr<M, 2, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+            if (f4 <= 4) return launch_xr<M, 4, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+            return launch_xr<M, 8, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
         }
-        return launch_sized<M, 0, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
     }
     // the activations fit in the registers of the workgroup's threads
     // (PRE variants are built for m <= 2, the decode sizes)
     const int pre_chunks = (M * k / 16 + kGemvThreads - 1) / kGemvThreads;
     const int pre = (M <= 2 && pre_chunks <= kActPre && M * nb <= kGemvThreads) ? pre_chunks : 0;
-    if (pre == 1) return launch_sized<M, (M <= 2 ? 1 : 0), false>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
-    if (pre == 2) return launch_sized<M, (M <= 2 ? 2 : 0), false>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
-    return launch_sized<M, 0, false>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+    if (pre == 1) return launch_xr<M, (M <= 2 ? 1 : 0), false>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+    if (pre == 2) return launch_xr<M, (M <= 2 ? 2 : 0), false>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+    return launch_xr<M, 0, false>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
 }
 
 // Shared checks and the dispatch on m; x == nullptr selects the q8_1 inputs.
@@ -559,6 +568,9 @@ static int gemv_entry(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, c
                       float *y, int m, int k, int n, void *stream) {
     if (m < 1 || m > BQM_GEMV_MAX_M || k < 256 || n < 1) return BQM_EINVAL;
     if (k % 256 != 0) return BQM_EUNSUPPORTED;
+    // in-kernel quantization is for decode: every workgroup quantizes the
+    // whole activation, which only pays while it fits in registers
+    if (x && (m > 2 || m * k > kActPreX * kGemvThreads * 4)) return BQM_EUNSUPPORTED;
     if (w_row_bytes < (int64_t)(k / kQK) * kQ80Bytes || w_row_bytes % 16 != 0) return BQM_EUNSUPPORTED;
     if (!aligned(w, 16) || !aligned(y, 4)) return BQM_EUNSUPPORTED;
     if (x ? !aligned(x, 16) : (!aligned(xq, 16) || !aligned(xds, 8))) return BQM_EUNSUPPORTED;

@@ -97,9 +97,11 @@ int bqm_q8_0_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const
  * followed by bqm_q8_0_gemv, with the quantization done by every workgroup
  * into its on-chip copy (same rule, same device code), so xq/xds never go
  * through memory.  y is bitwise equal to the two-call path.
- *   w, w_row_bytes, y, m, k, n : as bqm_q8_0_gemv (1 <= m <= 15, k % 256 == 0,
- *                                the same on-chip limit m*k*9/8 <= 98304).
+ *   w, w_row_bytes, y, k, n : as bqm_q8_0_gemv (k % 256 == 0).
  *   x : f32 activations [m][k], 16-byte aligned.
+ *   m : 1 or 2 with m*k <= 8192 (decode); 3 <= m <= 15 or a larger m*k gives
+ *       BQM_EUNSUPPORTED (every workgroup quantizes the whole activation,
+ *       which only pays while it fits in registers; use the two calls).
  * ("decode_kernel_census.rs" fn q8: the q8_1 activation of the m=1 Q8_0
  * GEMV; the pages run the quantizer as its own step.)
  */

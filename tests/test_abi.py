@@ -106,6 +106,8 @@ def test_gemv_f32_validation(L):
     assert f(A16, rb, B16, P(0x400002), 1, 4096, 8, NUL) == 2
     rb2 = 16384 // 32 * 34
     assert f(A16, rb2, B16, D16, 9, 16384, 8, NUL) == 2            # on-chip limit
+    assert f(A16, rb, B16, D16, 3, 4096, 8, NUL) == 2              # decode only: m <= 2
+    assert f(A16, rb2, B16, D16, 1, 16384, 8, NUL) == 2            # m*k <= 8192
 
 
 def test_gemv_m_range_and_on_chip_limit(L):
