@@ -19,10 +19,13 @@
 //  * The e4m3 GEMM's organisation: workgroup tile 128 x 64*NT, 8 waves of
 //    32 x 32*NT (two per SIMD), k staged 128 at a time (exactly one grid
 //    block) in double-buffered LDS with padded 144-byte rows, global loads
-//    two stages ahead in registers.
-//  * Per stage a wave runs two v_mfma_scale_f32_32x32x64_f8f6f4 (unit E8M0
-//    scales) per 32x32 tile into a block partial P started at zero, then
-//    folds acc += P * (xs[t] * g), two VALU ops per output element.  g is one
+//    two stages ahead in registers; NT (2..5) chosen per shape so the tiles
+//    fill whole rounds of the CUs (m=512, N=20480: NT=5, 256 tiles).
+//  * Per stage and 32x32 tile a wave runs two v_mfma_scale_f32_32x32x64_f8f6f4
+//    (unit E8M0 scales) into a block partial P started at zero and folds it
+//    at once, acc += P * (xs[t] * g), two VALU ops per output element; one
+//    partial at a time keeps NT=5 within 216 VGPRs, and the fold of one tile
+//    runs under the next tile's MFMAs.  g is one
 //    scalar per 32-column tile (a 32-aligned tile never straddles a 128-row
 //    block of the grid), read with scalar loads one stage ahead; the 128
 //    token scales of the stage go through LDS with the operand tiles.
@@ -221,21 +224,7 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + 16);
             return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         };
-        v8i a0 = ld8(pa), a1 = ld8(pa + 64);
-        v8i b0[NT], b1[NT];
-#pragma unroll
-        for (int j = 0; j < NT; j++) {
-            b0[j] = ld8(pb + j * 32 * kB8RowStride);
-            b1[j] = ld8(pb + j * 32 * kB8RowStride + 64);
-        }
-        v16f P[NT];
-        const v16f z = {0};
-#pragma unroll
-        for (int j = 0; j < NT; j++)
-            P[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0[j], z, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-        for (int j = 0; j < NT; j++)
-            P[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1[j], P[j], 0, 0, 0, 127, 0, 127);
+        const v8i a0 = ld8(pa), a1 = ld8(pa + 64);
         // token scales of the 16 output rows of this lane: rows
         // wm*32 + 8*(v/4) + 4*khalf + v%4, four consecutive per float4
         float sx[16];
@@ -247,10 +236,15 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
             sx[4 * i + 2] = q.z;
             sx[4 * i + 3] = q.w;
         }
+        const v16f z = {0};
 #pragma unroll
-        for (int j = 0; j < NT; j++)
+        for (int j = 0; j < NT; j++) {
+            const v8i b0 = ld8(pb + j * 32 * kB8RowStride), b1 = ld8(pb + j * 32 * kB8RowStride + 64);
+            v16f P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, z, 0, 0, 0, 127, 0, 127);
+            P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, P, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-            for (int v = 0; v < 16; v++) acc[j][v] = __builtin_fmaf(P[j][v], sx[v] * G[j], acc[j][v]);
+            for (int v = 0; v < 16; v++) acc[j][v] = __builtin_fmaf(P[v], sx[v] * G[j], acc[j][v]);
+        }
     };
 
     B8Regs<NT> R0, R1;
@@ -283,6 +277,22 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
             if (row < m) y[(int64_t)row * n + col] = acc[j][v];
         }
     }
+}
+
+// The tile width (NT) that needs the fewest rounds of workgroups over the
+// CUs, weighting each round by its width; ties go to the wider tile.
+static int b8_pick_nt(int m, int n, int cus) {
+    int best = 5;
+    int64_t best_cost = -1;
+    for (int nt = 5; nt >= 2; nt--) {
+        const int64_t tiles = (int64_t)((m + kB8BM - 1) / kB8BM) * ((n + 64 * nt - 1) / (64 * nt));
+        const int64_t cost = (tiles + cus - 1) / cus * nt;
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = nt;
+        }
+    }
+    return best;
 }
 
 template <int NT>
@@ -337,5 +347,11 @@ extern "C" int bqm_e4m3_blk_gemm(const uint8_t *w, const float *grid, const uint
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(grid, 4) || !aligned(xs, 4) || !aligned(y, 4))
         return BQM_EUNSUPPORTED;
     if ((int64_t)kB8BM * k > 0x7FFFFFF0ll || (int64_t)320 * k > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
-    return launch_b8<3>(w, grid, xq, xs, y, m, k, n, as_stream(stream));
+    hipStream_t s = as_stream(stream);
+    switch (b8_pick_nt(m, n, device_cus())) {
+        case 2: return launch_b8<2>(w, grid, xq, xs, y, m, k, n, s);
+        case 3: return launch_b8<3>(w, grid, xq, xs, y, m, k, n, s);
+        case 4: return launch_b8<4>(w, grid, xq, xs, y, m, k, n, s);
+        default: return launch_b8<5>(w, grid, xq, xs, y, m, k, n, s);
+    }
 }

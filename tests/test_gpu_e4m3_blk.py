@@ -107,8 +107,11 @@ def gemm_case(bqm, m, k, n, seed):
     return w, grid, xq, xs, y.cpu().numpy()
 
 
+# small shapes take NT=2 (64*NT output columns per workgroup), (128, 128,
+# 40000) NT=3, (256, 256, 30000) NT=4 on 256 compute units, the full-size
+# workload NT=5
 @pytest.mark.parametrize("m,k,n", [(1, 128, 1), (17, 256, 33), (130, 512, 300), (64, 4096, 640), (200, 1024, 129),
-                                   (3, 8192, 70), (256, 384, 1000)])
+                                   (3, 8192, 70), (256, 384, 1000), (128, 128, 40000), (256, 256, 30000)])
 def test_blk_gemm_matches_oracle(bqm, m, k, n):
     w, grid, xq, xs, y = gemm_case(bqm, m, k, n, seed=m + k + n)
     y_ref, T = oracle.e4m3_blk_matmul(w, grid, xq, xs)
