@@ -26,8 +26,9 @@
 //    in LDS with each chunk's four 16-byte pieces rotated by (c + c/4) % 4, so
 //    the 16 lanes of a read phase, on 16 consecutive chunks, hit distinct
 //    banks.  More than 4 tokens run as several token groups; the groups of
-//    the same rows are adjacent workgroups, so their re-reads of a weight
-//    tile meet in the Infinity Cache.
+//    the same rows run together on one XCD, so their re-reads of a weight
+//    tile are served by that XCD's L2.  Past 4 tokens the kernel is bound by
+//    its f32 FMAs (one per weight byte and token), not by memory.
 //  * Arithmetic: per chunk and token, 16 fma in k order into one f32 partial
 //    per lane; the L partials of a row are summed by a fixed DPP /
 //    permlane-swap butterfly; y = w_scale * sum.  A token's operation order
@@ -51,6 +52,7 @@ struct E8Geom {
     int J;         // chunks per lane per row
     int n_items;   // ceil(n / G)
     int ngroups;   // token groups
+    int xcd_map;   // token groups of the same rows on one XCD (see the kernel)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t e8_rsrc(const void *base, uint32_t bytes) {
@@ -83,8 +85,19 @@ __global__ __launch_bounds__(kE8Threads) void e4m3_gemv_kernel(const uint8_t *__
     extern __shared__ __attribute__((aligned(16))) float xs[];   // [TG][k], pieces rotated
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tg = blockIdx.x % g.ngroups;
-    const int rwg = blockIdx.x / g.ngroups;
+    // With several token groups, the groups that stream the same rows are
+    // placed on one XCD (workgroups reach the 8 XCDs round-robin, id % 8) at
+    // consecutive slots, so they run together and all but the first read
+    // the weights from that XCD's L2 instead of from memory.
+    int tg, rwg;
+    if (g.xcd_map) {
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        tg = slot % g.ngroups;
+        rwg = (slot / g.ngroups) * 8 + xcd;
+    } else {
+        tg = blockIdx.x % g.ngroups;
+        rwg = blockIdx.x / g.ngroups;
+    }
     const int t0 = tg * TG;
     const int tcount = min(TG, m - t0);
     const int nwaves = (gridDim.x / g.ngroups) * kE8Waves;
@@ -249,8 +262,14 @@ static int e8_launch(const uint8_t *w, const float *x, float w_scale, float *y, 
     if (cap < 1) cap = 1;
     if (rwgs > cap) rwgs = cap;
     if (rwgs < 1) rwgs = 1;
+    E8Geom gg = g;
+    gg.xcd_map = 0;
+    if (g.ngroups > 1 && rwgs >= 8) {
+        rwgs -= rwgs % 8;   // every XCD holds whole sets of token groups
+        gg.xcd_map = 1;
+    }
     hipLaunchKernelGGL((e4m3_gemv_kernel<TG, JM, XREG>), dim3(rwgs * g.ngroups), dim3(kE8Threads), lds, stream, w, x,
-                       w_scale, y, m, k, n, g);
+                       w_scale, y, m, k, n, gg);
     return launch_status();
 }
 
