@@ -45,7 +45,13 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA
 FP8_PEAK_TFLOPS = 5000.0         # dense fp8 MFMA
 FP16_PEAK_TFLOPS = 2500.0        # dense fp16 MFMA
-ROTATE = 3
+ROTATE = 3                       # weight copies for the 280 MB head (841 MB rotated)
+ROTATE_BYTES = 600_000_000       # smaller weights: copies enough for >= 600 MB, past the 256 MB cache
+
+
+def copies_for(nbytes: int) -> int:
+    """Weight copies to rotate so that every launch streams its weights from HBM."""
+    return max(ROTATE, min(64, -(-ROTATE_BYTES // nbytes)))
 
 
 def q8_0_bytes(m, k, n):
@@ -92,19 +98,24 @@ def timed_loop(torch, stream, steps, fns):
         torch.cuda.synchronize()
         return g
 
-    def replay_ms(g):
+    def replay_ms(g, reps=1):
         rs = torch.cuda.current_stream()
         g.replay()                          # warm replay
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(rs)
-        g.replay()
-        b.record(rs)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b)
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(rs)
+            g.replay()
+            b.record(rs)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        return sorted(times)[len(times) // 2]
 
+    # the step loop: exactly `steps` passes, timed once; each kernel: the
+    # median of 9 replays of `steps` back-to-back launches
     total_ms = replay_ms(capture([fn for _, fn in fns]))
-    per = {name: replay_ms(capture([fn])) / steps for name, fn in fns}
+    per = {name: replay_ms(capture([fn]), reps=9) / steps for name, fn in fns}
     return total_ms, per
 
 
@@ -240,10 +251,11 @@ def main():
         for n in workloads.GEMM_NS:
             log(f"[bench] mmq n={n}")
             w0 = torch.from_numpy(workloads.q8_0_weights(n, k, rng)).to(dev)
-            ws = [w0] + [w0.clone() for _ in range(ROTATE - 1)]
+            nc = copies_for(w0.numel())
+            ws = [w0] + [w0.clone() for _ in range(nc - 1)]
             y = torch.empty((m, n), dtype=torch.float32, device=dev)
             fns = [("quantize", lambda s: bqm.bqm_q8_1_quantize(x, xq, xds)),
-                   ("gemm", lambda s: bqm.bqm_q8_0_gemm(ws[s % ROTATE], xq, xds, y))]
+                   ("gemm", lambda s: bqm.bqm_q8_0_gemm(ws[s % nc], xq, xds, y))]
             timed_loop(torch, stream, args.warmup, fns)
             total_ms, per = timed_loop(torch, stream, args.steps, fns)
             ops = 2.0 * m * n * k
@@ -263,13 +275,14 @@ def main():
         log("[bench] e4m3 n=20480")
         codes, w_scale = workloads.e4m3_weights(n, k, rng)
         w0 = torch.from_numpy(codes).to(dev)
-        ws = [w0] + [w0.clone() for _ in range(ROTATE - 1)]
+        nc = copies_for(w0.numel())
+        ws = [w0] + [w0.clone() for _ in range(nc - 1)]
         x = torch.from_numpy(workloads.activations(m, k, rng)).to(dev)
         xq8 = torch.empty((m, k), dtype=torch.uint8, device=dev)
         sc = torch.empty(4, dtype=torch.float32, device=dev)
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         fns = [("quantize", lambda s: bqm.bqm_e4m3_quantize_amax(x, w_scale, xq8, sc)),
-               ("gemm", lambda s: bqm.bqm_e4m3_gemm(ws[s % ROTATE], xq8, sc, y))]
+               ("gemm", lambda s: bqm.bqm_e4m3_gemm(ws[s % nc], xq8, sc, y))]
         timed_loop(torch, stream, args.warmup, fns)
         total_ms, per = timed_loop(torch, stream, args.steps, fns)
         ops = 2.0 * m * n * k
@@ -309,17 +322,18 @@ def main():
         m, k, n = 512, 4096, 20480
         log("[bench] f16 mirror n=20480")
         wq = torch.from_numpy(workloads.q8_0_weights(n, k, rng)).to(dev)
-        w16s = [torch.empty((n, k), dtype=torch.float16, device=dev) for _ in range(ROTATE)]
+        nc = copies_for(2 * n * k)
+        w16s = [torch.empty((n, k), dtype=torch.float16, device=dev) for _ in range(nc)]
         for w16 in w16s:
             bqm.bqm_q8_0_dequant_f16(wq, k, w16)
         x = torch.from_numpy(workloads.activations(m, k, rng, outliers=True)).to(dev)
         x16 = torch.empty((m, k), dtype=torch.float16, device=dev)
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         fns = [("cvt", lambda s: bqm.bqm_f16_cvt(x, x16)),
-               ("gemm", lambda s: bqm.bqm_f16_gemm(w16s[s % ROTATE], x16, y))]
+               ("gemm", lambda s: bqm.bqm_f16_gemm(w16s[s % nc], x16, y))]
         timed_loop(torch, stream, args.warmup, fns)
         total_ms, per = timed_loop(torch, stream, args.steps, fns)
-        dq = [("dequant", lambda s: bqm.bqm_q8_0_dequant_f16(wq, k, w16s[s % ROTATE]))]
+        dq = [("dequant", lambda s: bqm.bqm_q8_0_dequant_f16(wq, k, w16s[s % nc]))]
         timed_loop(torch, stream, 2, dq)
         _, per_dq = timed_loop(torch, stream, args.steps, dq)
         ops = 2.0 * m * n * k
@@ -341,18 +355,19 @@ def main():
         log("[bench] e4m3 block-128 n=20480")
         codes, grid_h = workloads.e4m3_blk_weights(n, k, rng)
         w0 = torch.from_numpy(codes).to(dev)
-        ws = [w0] + [w0.clone() for _ in range(ROTATE - 1)]
+        nc = copies_for(w0.numel())
+        ws = [w0] + [w0.clone() for _ in range(nc - 1)]
         grid = torch.from_numpy(grid_h).to(dev)
         x = torch.from_numpy(workloads.activations(m, k, rng, outliers=True)).to(dev)
         xq8 = torch.empty((m, k), dtype=torch.uint8, device=dev)
         xs = torch.empty((m, k // 128), dtype=torch.float32, device=dev)
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         fns = [("quantize", lambda s: bqm.bqm_e4m3_blk_quantize(x, xq8, xs)),
-               ("gemm", lambda s: bqm.bqm_e4m3_blk_gemm(ws[s % ROTATE], grid, xq8, xs, y))]
+               ("gemm", lambda s: bqm.bqm_e4m3_blk_gemm(ws[s % nc], grid, xq8, xs, y))]
         timed_loop(torch, stream, args.warmup, fns)
         total_ms, per = timed_loop(torch, stream, args.steps, fns)
         cnt = torch.empty(1, dtype=torch.int64, device=dev)
-        scan = [("nan_scan", lambda s: bqm.bqm_e4m3_nan_count(ws[s % ROTATE], cnt))]
+        scan = [("nan_scan", lambda s: bqm.bqm_e4m3_nan_count(ws[s % nc], cnt))]
         timed_loop(torch, stream, 2, scan)
         _, per_scan = timed_loop(torch, stream, args.steps, scan)
         ops = 2.0 * m * n * k
@@ -433,6 +448,23 @@ def main():
                                "kind": "oracle",
                                "sample": f"the full decode-head step (q8_1 quantize + Q8_0 matmul, m=1, "
                                          f"K=4096, N=64448) repeated {reps} times in {t_total:.1f} s"}
+        # the same on one thread, in a child process (OpenMP fixes its team at start)
+        import subprocess
+        code = ("import sys, time, numpy as np; sys.path.insert(0, %r); import oracle, workloads\n"
+                "w = workloads.q8_0_weights(64448, 4096, np.random.default_rng(0))\n"
+                "x = workloads.activations(1, 4096, np.random.default_rng(1))\n"
+                "r, t0 = 0, time.perf_counter()\n"
+                "while time.perf_counter() - t0 < 5.0:\n"
+                "    q, d = oracle.q8_1_quantize(x); oracle.q8_0_matmul(w, q, d, 4096); r += 1\n"
+                "print(r, time.perf_counter() - t0)\n") % ROOT
+        try:
+            res = subprocess.run([sys.executable, "-c", code], env={**os.environ, "OMP_NUM_THREADS": "1"},
+                                 capture_output=True, text=True, timeout=120)
+            r1, t1 = res.stdout.split()
+            out["cpu_baseline"]["single_thread_value"] = round(
+                int(r1) * (q8_0_bytes(m, k, n) + m * k * 4) / float(t1) / 1e9, 2)
+        except (subprocess.SubprocessError, ValueError, OSError):
+            out["cpu_baseline"]["single_thread_value"] = None
 
     print(json.dumps(out), flush=True)
 
