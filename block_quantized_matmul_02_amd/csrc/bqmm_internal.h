@@ -37,6 +37,12 @@ inline int device_cus() {
     return cus;
 }
 
+// The matrix-core GEMV for 3..15 tokens (q8_0_gemv_mma.hip): whether it takes
+// a shape, and its launch (arguments already checked by the GEMV entry).
+bool gemv_mma_applies(int m, int k, int n);
+int gemv_mma(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y, int m, int k, int n,
+             hipStream_t s);
+
 // ---------------------------------------------------------------- device side
 
 // IEEE binary16 bits -> f32 (exact; hardware conversion handles subnormals).

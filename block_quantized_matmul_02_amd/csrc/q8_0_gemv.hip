@@ -578,6 +578,8 @@ static int gemv_entry(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, c
     if (x ? !aligned(x, 16) : (!aligned(xq, 16) || !aligned(xds, 8))) return BQM_EUNSUPPORTED;
     if ((int64_t)m * k * 9 / 8 > kActLdsMax) return BQM_EUNSUPPORTED;
     if (w_row_bytes > 0x7FFFFFFF / 64) return BQM_EUNSUPPORTED;
+    // 3..15 tokens on the matrix cores (same per-row order as below)
+    if (!x && gemv_mma_applies(m, k, n)) return gemv_mma(w, w_row_bytes, xq, xds, y, m, k, n, as_stream(stream));
     GemvGeom g;
     if (!make_geom(k, n, w_row_bytes, g)) return BQM_EUNSUPPORTED;
     // the per-slot offsets r*w_row_bytes + 16*col must fit in 32 bits
