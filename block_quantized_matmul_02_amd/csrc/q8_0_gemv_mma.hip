@@ -133,6 +133,11 @@ __global__ __launch_bounds__(kMvThreads) void q8_0_gemv_mma_kernel(const uint8_t
         // pieces past the chunk land in the never-read 16 bytes at the end of the tile
         loff[s] = ok ? (uint32_t)(r * kMvTileStride + 16 * col) : (uint32_t)(kMvRows * kMvTileStride);
     }
+    // Materialize the offsets here, before any load is in flight: computed
+    // later, their 64-bit arithmetic was placed in registers next to pending
+    // load results and waited for them.
+#pragma unroll
+    for (int s = 0; s < kMvSlots; s++) asm volatile("" ::"v"(voff[s]), "v"(loff[s]));
 
     // Issue the loads of iteration i; past the last one the resource is empty.
     auto issue = [&](u32x4 (&buf)[kMvSlots], int i) {
@@ -249,28 +254,51 @@ __global__ __launch_bounds__(kMvThreads) void q8_0_gemv_mma_kernel(const uint8_t
         finish(i, cb);
     };
 
+    // Activations first: at most two (token, pair) items per thread (m*K/64 <=
+    // 15*64 <= 2*512), loaded before the weight chunks so that waiting for
+    // them does not wait for the chunks too, then written to LDS permuted for
+    // the B operand (see the head of the file).  Items past the activations
+    // load from past the resources (zeros) and are not written.
+    const __amdgpu_buffer_rsrc_t rq = mv_rsrc(xq, (uint32_t)(M * k));
+    const __amdgpu_buffer_rsrc_t rd = mv_rsrc(xds, (uint32_t)(M * g.nb * 8));
+    u32x4 ac[2][4], ad[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int e = (int)threadIdx.x + kMvThreads * h;
+        const int t = e / g.P, p = e - (e / g.P) * g.P;
+        const bool ok = e < M * g.P;
+        const uint32_t qo = ok ? (uint32_t)(t * k + 64 * p) : (uint32_t)(M * k);
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+            ac[h][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, qo + 16 * c, 0, 0));
+        ad[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rd, ok ? (uint32_t)((t * g.nb + 2 * p) * 8) : (uint32_t)(M * g.nb * 8), 0, 0));
+    }
     u32x4 bufA[kMvSlots], bufB[kMvSlots];
     issue(bufA, 0);
     issue(bufB, 1);
-    // Activations, permuted for the B operand (see the head of the file).
-    for (int e = threadIdx.x; e < M * g.P; e += kMvThreads) {
-        const int t = e / g.P, p = e - (e / g.P) * g.P;
-        const u32x4 c0 = *reinterpret_cast<const u32x4 *>(xq + (int64_t)t * k + 64 * p);
-        const u32x4 c1 = *reinterpret_cast<const u32x4 *>(xq + (int64_t)t * k + 64 * p + 16);
-        const u32x4 c2 = *reinterpret_cast<const u32x4 *>(xq + (int64_t)t * k + 64 * p + 32);
-        const u32x4 c3 = *reinterpret_cast<const u32x4 *>(xq + (int64_t)t * k + 64 * p + 48);
-        uint8_t *dst = act_q + t * g.ts + 64 * p;
-        #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            u32x4 v;
-            v[0] = c0[q];
-            v[1] = c1[q];
-            v[2] = c2[q];
-            v[3] = c3[q];
-            *reinterpret_cast<u32x4 *>(dst + 16 * q) = v;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int e = (int)threadIdx.x + kMvThreads * h;
+        if (e < M * g.P) {
+            const int t = e / g.P, p = e - (e / g.P) * g.P;
+            uint8_t *dst = act_q + t * g.ts + 64 * p;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                u32x4 v;
+                v[0] = ac[h][0][q];
+                v[1] = ac[h][1][q];
+                v[2] = ac[h][2][q];
+                v[3] = ac[h][3][q];
+                *reinterpret_cast<u32x4 *>(dst + 16 * q) = v;
+            }
+            // each element is copied to a scalar before the bit cast: clang
+            // lowers a bit cast of a vector-element expression to a read of
+            // element 0
+            const uint32_t d0 = ad[h][0], d1 = ad[h][2];
+            act_d[t * g.ds + 2 * p] = __builtin_bit_cast(float, d0);
+            act_d[t * g.ds + 2 * p + 1] = __builtin_bit_cast(float, d1);
         }
-        act_d[t * g.ds + 2 * p] = xds[2 * (int64_t)(t * g.nb + 2 * p)];
-        act_d[t * g.ds + 2 * p + 1] = xds[2 * (int64_t)(t * g.nb + 2 * p + 1)];
     }
     __syncthreads();
     // Both halves of the loop body always run, so on every path into a stage
