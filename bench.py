@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--sweep-shapes", default=None,
+                    help="comma-separated KxN shapes for the decode/verify sweep (default: all four)")
     ap.add_argument("--only", choices=["gemv", "sweep", "mmq", "e4m3", "e4m3_gemv", "f16", "accprobe", "e4m3_blk", "copy"], default=None,
                     help="run one part only (for profiler passes); 'copy' runs a plain 1 GiB device copy "
                          "that calibrates the HBM byte counters")
@@ -207,7 +209,10 @@ def main():
     # ---------------------------------------------------------------- decode / verify sweep
     if args.only in (None, "sweep"):
         sweep = {}
-        for k, n in workloads.GEMV_SWEEP_SHAPES:
+        shapes = workloads.GEMV_SWEEP_SHAPES
+        if args.sweep_shapes:
+            shapes = [tuple(int(v) for v in s.split("x")) for s in args.sweep_shapes.split(",")]
+        for k, n in shapes:
             w0 = torch.from_numpy(workloads.q8_0_weights(n, k, rng)).to(dev)
             copies = max(3, -(-600_000_000 // w0.numel()))        # rotate >= 600 MB past the 256 MB cache
             ws = [w0] + [w0.clone() for _ in range(copies - 1)]

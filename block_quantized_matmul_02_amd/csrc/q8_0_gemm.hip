@@ -10,11 +10,11 @@
 //  * v_mfma_i32_32x32x32_i8 has K = 32, exactly one Q8_0 block, so one MFMA
 //    gives the int32 block sums S of a 32x32 output tile.
 //  * The fold is per output element and block: acc = fma(float(S),
-//    d_x * d_w, acc), three VALU ops.  Without packed f32 the VALU retires a
-//    wave64 op every 4 clk, so the fold (192 clk per 32x32 tile and block)
-//    bounds the kernel and the MFMA (about 37 clk) hides under it; measured on
-//    MI355X, an int8 MFMA plus this fold per block runs at 190 clk.  The
-//    MFMA of block b+1 is issued before the fold of block b, and the LDS
+//    d_x * d_w, acc).  The scale products come from the matrix core (see
+//    compute_stage), which leaves two VALU ops per element and block.
+//    Without packed f32 the VALU retires a wave64 op every 4 clk, so the fold
+//    takes 128 clk per 32x32 tile and block against about 32 clk of int8 MFMA.
+//    The MFMA of block b+1 is issued before the fold of block b, and the LDS
 //    operands are read two blocks ahead, so the matrix core, the LDS and the
 //    VALU overlap.  MFMA results stay in ordinary VGPRs (the build asks for
 //    the VGPR form), so the fold reads them without copies.
@@ -37,8 +37,7 @@
 //  * Quant tiles are stored with a padded row stride of 272 bytes (256 + 16),
 //    so the MFMA operand reads of 8 consecutive rows at the same k hit
 //    distinct banks and every LDS address is a per-lane base plus a
-//    compile-time offset; the scale reads of the fold are broadcasts (every
-//    lane of a half-wave reads the same four rows).
+//    compile-time offset.
 //  * Global loads are range-checked buffer loads: ragged m and n tails read
 //    zeros (zero scales), and only in-range outputs are stored.
 //
