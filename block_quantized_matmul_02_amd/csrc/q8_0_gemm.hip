@@ -69,7 +69,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mmq_rsrc(const void *base, int
 template <int BM>
 struct MmqStage {
     uint8_t x[BM * kMmqRowStride];       // activation quants, padded rows
-    uint8_t w[kMmqBN * kMmqRowStride];   // weight quants, padded rows
+    uint8_t w[kMmqBN * kMmqRowStride];   // weight quants, padded rows: first halves of the 8 blocks, then second halves
     // d_x / d_w per block and row.  A row of blocks is padded by 4 floats:
     // the stores write 8 blocks of 4 (d_w) or 8 (d_x) rows per 32 lanes, and a
     // ds_write_b32 serves 32 lanes from 32 banks of 4 bytes, so block rows
@@ -198,10 +198,14 @@ __global__ __launch_bounds__(4 * BM) void q8_0_gemm_kernel(const uint8_t *__rest
             qa1[1] = __builtin_amdgcn_alignbit(d[6], d[5], 16u);
             qa1[2] = __builtin_amdgcn_alignbit(d[7], d[6], 16u);
             qa1[3] = __builtin_amdgcn_alignbit(d[8], d[7], 16u);
+            // weight tile rows hold the first 16 bytes of blocks 0..7, then the
+            // second 16 bytes of blocks 0..7: the 8 lanes of a row then store
+            // 128 consecutive bytes per instruction (block-contiguous rows
+            // made these stores 4-way bank-conflicted)
             const int b = 2 * wpair[j] + odd[j];
-            uint8_t *wr = S.w + wrow[j] * kMmqRowStride + 32 * b;
-            *reinterpret_cast<u32x4 *>(wr + 0) = odd[j] ? R.w[j][0] : qa0;
-            *reinterpret_cast<u32x4 *>(wr + 16) = odd[j] ? R.w[j][1] : qa1;
+            uint8_t *wr = S.w + wrow[j] * kMmqRowStride + 16 * b;
+            *reinterpret_cast<u32x4 *>(wr) = odd[j] ? R.w[j][0] : qa0;
+            *reinterpret_cast<u32x4 *>(wr + 128) = odd[j] ? R.w[j][1] : qa1;
             S.dw[b][wrow[j]] = half_bits_to_float(odd[j] ? (R.w8[j] >> 16) : (d[0] & 0xFFFFu));
         }
 #pragma unroll
@@ -231,10 +235,10 @@ __global__ __launch_bounds__(4 * BM) void q8_0_gemm_kernel(const uint8_t *__rest
     auto compute_stage = [&](const Stage &S) {
         v4i A[3], B[3];
         const uint8_t *xa = S.x + arow * kMmqRowStride + 16 * khalf;
-        const uint8_t *wb = S.w + brow * kMmqRowStride + 16 * khalf;
+        const uint8_t *wb = S.w + brow * kMmqRowStride + 128 * khalf;
         auto rd = [&](int b, int slot) {
             A[slot] = *reinterpret_cast<const v4i *>(xa + 32 * b);
-            B[slot] = *reinterpret_cast<const v4i *>(wb + 32 * b);
+            B[slot] = *reinterpret_cast<const v4i *>(wb + 16 * b);
         };
         // scale operands of the 4 block pairs: d_x[b + khalf][token], d_w[b + khalf][weight row]
         float SA[kMmqBlocks / 2], SB[kMmqBlocks / 2];
