@@ -32,7 +32,7 @@
 namespace bqm {
 
 constexpr int kAmaxThreads = 256;
-constexpr int kAmaxMaxBlocks = 512;
+constexpr int kAmaxMaxBlocks = 2048;
 
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
@@ -58,8 +58,18 @@ __global__ __launch_bounds__(kAmaxThreads) void e4m3_amax_partial_kernel(const f
                                                                          int64_t count, float *__restrict__ partial) {
     __shared__ float red[kAmaxThreads / 64];
     float a = 0.0f;
+    // four independent 16-byte loads in flight per thread and step
     const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < nvec; i += stride) {
+    int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    for (; i + 3 * stride < nvec; i += 4 * stride) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) v[u] = x[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            a = fmaxf(a, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
+    }
+    for (; i < nvec; i += stride) {
         float4 v = x[i];
         a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
@@ -96,12 +106,20 @@ __global__ __launch_bounds__(256) void e4m3_quantize_kernel(const float4 *__rest
                                                             unsigned *__restrict__ xq) {
     const float mul = scales[1];
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride) {
-        float4 v = x[i];
+    auto q4 = [&](float4 v) {
         int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v.x * mul), clamp448(v.y * mul), 0, false);
-        int both = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v.z * mul), clamp448(v.w * mul), lo, true);
-        xq[i] = (unsigned)both;
+        return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v.z * mul), clamp448(v.w * mul), lo, true);
+    };
+    // four independent 16-byte loads in flight per thread and step
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < nvec; i += 4 * stride) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) v[u] = x[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 4; u++) xq[i + u * stride] = q4(v[u]);
     }
+    for (; i < nvec; i += stride) xq[i] = q4(x[i]);
 }
 
 // ------------------------------------------------------------------ GEMM
@@ -312,7 +330,7 @@ extern "C" int bqm_e4m3_quantize_amax(const float *x, uint8_t *xq, float *scales
     const int64_t count = (int64_t)m * k;
     const int64_t nvec = count / 4;
     // partials live in xq: nblocks floats must fit in count bytes
-    int64_t nblocks = (nvec + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
+    int64_t nblocks = (nvec + kAmaxThreads * 4 - 1) / (kAmaxThreads * 4);
     if (nblocks > kAmaxMaxBlocks) nblocks = kAmaxMaxBlocks;
     if (nblocks > count / 4) nblocks = count / 4;
     if (nblocks < 1) nblocks = 1;
