@@ -20,29 +20,39 @@
 //    arithmetic, with no LDS pass.
 //  * Decode: v_cvt_pk_f32_fp8 turns two OCP e4m3 bytes into two exact f32
 //    values (every e4m3 value is exact in f32).
-//  * Activations: for one token and k <= 4096 a lane's chunks are the same on
-//    every row, so their 16*J values sit in registers, loaded before the
-//    first weight tiles.  Otherwise a token group (up to 4 tokens) is staged
-//    in LDS with each chunk's four 16-byte pieces rotated by (c + c/4) % 4, so
-//    the 16 lanes of a read phase, on 16 consecutive chunks, hit distinct
-//    banks.  More than 4 tokens run as several token groups; the groups of
-//    the same rows run together on one XCD, so their re-reads of a weight
-//    tile are served by that XCD's L2.  Past 4 tokens the kernel is bound by
-//    its f32 FMAs (one per weight byte and token), not by memory.
-//  * Arithmetic: per chunk and token, 16 fma in k order into one f32 partial
-//    per lane; the L partials of a row are summed by a fixed DPP /
-//    permlane-swap butterfly; y = w_scale * sum.  A token's operation order
-//    does not depend on m or its group, so decode and verify agree bitwise.
+//  * Per-row order, the same for every token count: a leaf is 16 fma over one
+//    chunk in k order, starting from +0; a lane sums its J slot leaves by the
+//    perfect binary tree over the slot index (padded with +0 to a power of
+//    two); the L lane sums are added by a fixed DPP / permlane-swap butterfly,
+//    the perfect binary tree over the lane index; y = w_scale * sum.  A leaf
+//    is never -0, so the +0 padding changes nothing, and decode and verify
+//    agree bitwise whatever the kernel below.  Rounding: at most 16 fma, 3
+//    slot levels and 6 lane levels per output, (16 + 9) * 2^-24 of
+//    sum|terms|.
+//  * One token (k <= 4096): a lane's chunks are the same on every row, so
+//    their 16*J activations sit in registers, loaded before the first weight
+//    tiles.
+//  * Two or more tokens at k > 1024 (J >= 2): the slot-split kernel below,
+//    with each wave owning one chunk slot and the tokens' values of that
+//    chunk in registers.
+//  * Otherwise (k <= 1024, or a launch too large for 32-bit output offsets)
+//    the tokens are staged in LDS, one workgroup-shared copy per token group
+//    (as many tokens as the LDS holds), each chunk's four 16-byte pieces
+//    rotated by (c + c/4) % 4 so the 16 lanes of a read phase, on 16
+//    consecutive chunks, hit distinct banks.  Token groups of the same rows
+//    run together on one XCD, so their re-reads of a weight tile are served
+//    by that XCD's L2.
 #include "bqmm_internal.h"
 
 namespace bqm {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kE8Threads = 256;
-constexpr int kE8Waves = kE8Threads / 64;
-constexpr int kE8MaxTG = 4;          // tokens per group
+constexpr int kE8Threads = 256;       // workgroup for one and two tokens
+constexpr int kE8GroupThreads = 512;  // workgroup for three or more tokens
+constexpr int kE8SlotsMinM = 2;       // fewest tokens for the slot-split kernel
 constexpr int kE8MaxK = 8192;
+constexpr int kE8LdsBytes = 160 * 1024;
 
 struct E8Geom {
     int CPR;       // 16-byte chunks per row
@@ -51,6 +61,7 @@ struct E8Geom {
     int G;         // rows per item
     int J;         // chunks per lane per row
     int n_items;   // ceil(n / G)
+    int tgsz;      // tokens per group (the last group may hold fewer)
     int ngroups;   // token groups
     int xcd_map;   // token groups of the same rows on one XCD (see the kernel)
 };
@@ -75,10 +86,33 @@ __device__ __forceinline__ void e8_decode16(const u32x4 c, float (&f)[16]) {
 // float offset of piece i (four floats) of chunk c inside a staged token row
 __device__ __forceinline__ int e8_piece(int c, int i) { return 16 * c + 4 * ((i + c + (c >> 2)) & 3); }
 
-// TG: token-group capacity; JM: chunk slots per lane (>= J); XREG: one token,
-// activations in registers.
-template <int TG, int JM, bool XREG>
-__global__ __launch_bounds__(kE8Threads) void e4m3_gemv_kernel(const uint8_t *__restrict__ w,
+// Perfect binary tree over N (a power of two) values in index order.  Slots
+// past a row's last chunk hold +0, and a chain that starts from +0 never ends
+// at -0, so padding with +0 to any larger power of two gives the same value.
+template <int N>
+__device__ __forceinline__ float e8_tree(const float *v) {
+    if constexpr (N == 1) return v[0];
+    else return e8_tree<N / 2>(v) + e8_tree<N / 2>(v + N / 2);
+}
+
+// Sum of one value over the L lanes of a row (lanes li = 0..L-1 of a group
+// of L): the perfect binary tree over li, formed by a fixed DPP /
+// permlane-swap butterfly (xor 1, xor 2, half-row mirror, row mirror, then
+// rows and halves swapped).
+__device__ __forceinline__ float e8_row_sum(float v, int L) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    if (L >= 32) v = swap16_sum(v);
+    if (L >= 64) v = swap32_sum(v);
+    return v;
+}
+
+// JM: chunk slots per lane (>= J); XREG: one token, activations in registers;
+// NT: threads per workgroup (all of them share the staged tokens).
+template <int JM, bool XREG, int NT>
+__global__ __launch_bounds__(NT) void e4m3_gemv_kernel(const uint8_t *__restrict__ w,
                                                              const float *__restrict__ x, float w_scale,
                                                              float *__restrict__ y, int m, int k, int n,
                                                              E8Geom g) {
@@ -98,10 +132,10 @@ __global__ __launch_bounds__(kE8Threads) void e4m3_gemv_kernel(const uint8_t *__
         tg = blockIdx.x % g.ngroups;
         rwg = blockIdx.x / g.ngroups;
     }
-    const int t0 = tg * TG;
-    const int tcount = min(TG, m - t0);
-    const int nwaves = (gridDim.x / g.ngroups) * kE8Waves;
-    const int wid = rwg * kE8Waves + wave;
+    const int t0 = tg * g.tgsz;
+    const int tcount = min(g.tgsz, m - t0);
+    const int nwaves = (gridDim.x / g.ngroups) * (NT / 64);
+    const int wid = rwg * (NT / 64) + wave;
     const int Q = wid < g.n_items ? (g.n_items - 1 - wid) / nwaves + 1 : 0;
 
     const int li = lane & (g.L - 1);
@@ -147,53 +181,86 @@ __global__ __launch_bounds__(kE8Threads) void e4m3_gemv_kernel(const uint8_t *__
             buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[j], 0, 2));
     };
 
+    // one token's lane partials summed over the row's L lanes, then scaled
+    auto finish = [&](float v, int t, int row, bool store) {
+        v = e8_row_sum(v, g.L);
+        if (store && li == 0 && row < n) y[(int64_t)(t0 + t) * n + row] = w_scale * v;
+    };
+
+    // No branch on a slot's validity: an invalid slot's weights are the zeros
+    // of an out-of-range load (its activations zeros too, or chunk 0 from
+    // LDS), so it adds exact zeros; a branch here would let the compiler sink
+    // the activation loads behind the tiles.
     auto compute = [&](const u32x4 (&buf)[JM], int q) {
-        float acc[TG];
+        const int row = (wid + nwaves * q) * g.G + gr;
+        if (XREG) {
+            float lf[JM];
 #pragma unroll
-        for (int t = 0; t < TG; t++) acc[t] = 0.0f;
-        // No branch on the slot's validity: an invalid slot's weights are the
-        // zeros of an out-of-range load (its activations zeros too, or chunk 0
-        // from LDS), so it adds exact zeros; a branch here would let the
-        // compiler sink the activation loads behind the tiles.
+            for (int j = 0; j < JM; j++) {
+                float f[16];
+                e8_decode16(buf[j], f);
+                lf[j] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < JM; j++) {
-            float f[16];
-            e8_decode16(buf[j], f);
-            const int c = valid[j] ? li + g.L * j : 0;
+                for (int e = 0; e < 16; e++) lf[j] = __builtin_fmaf(xr[XREG ? j : 0][e], f[e], lf[j]);
+            }
+            finish(e8_tree<JM>(lf), 0, row, true);
+            return;
+        }
+        // Staged tokens, two at a time (the second repeats the first when the
+        // group's count is odd, and is not stored), each with its slot leaves
+        // and trees as above.  Up to 4 slots the chunks are decoded once for
+        // all tokens.
+        constexpr bool PRE = JM <= 4;
+        float fw[PRE ? JM : 1][16];
+        if (PRE) {
 #pragma unroll
-            for (int t = 0; t < TG; t++) {
-                if (!XREG && t >= tcount) break;
-                float xv[16];
-                if (XREG) {
+            for (int j = 0; j < JM; j++) e8_decode16(buf[j], fw[PRE ? j : 0]);
+        }
+#pragma unroll 1
+        for (int t = 0; t < tcount; t += 2) {
+            const int t1 = t + 1 < tcount ? t + 1 : t;
+            const float *x0 = xs + t * k, *x1 = xs + t1 * k;
+            // activations of slot j+1 are read while slot j is computed; the
+            // scheduling barriers keep the compiler from reading every slot
+            // ahead (which needs 64 registers per slot and token pair)
+            float v0[2][16], v1[2][16];
+            auto fetch = [&](int j, float (&d0)[16], float (&d1)[16]) {
+                const int c = valid[j] ? li + g.L * j : 0;
 #pragma unroll
-                    for (int e = 0; e < 16; e++) xv[e] = xr[XREG ? j : 0][e];
+                for (int i = 0; i < 4; i++) {
+                    const float4 p0 = *reinterpret_cast<const float4 *>(x0 + e8_piece(c, i));
+                    const float4 p1 = *reinterpret_cast<const float4 *>(x1 + e8_piece(c, i));
+                    d0[4 * i + 0] = p0.x; d0[4 * i + 1] = p0.y; d0[4 * i + 2] = p0.z; d0[4 * i + 3] = p0.w;
+                    d1[4 * i + 0] = p1.x; d1[4 * i + 1] = p1.y; d1[4 * i + 2] = p1.z; d1[4 * i + 3] = p1.w;
+                }
+            };
+            fetch(0, v0[0], v1[0]);
+            float a0[JM], a1[JM];
+#pragma unroll
+            for (int j = 0; j < JM; j++) {
+                a0[j] = 0.0f;
+                a1[j] = 0.0f;
+                if (j + 1 < JM) fetch(j + 1 < JM ? j + 1 : j, v0[(j + 1) & 1], v1[(j + 1) & 1]);
+                float f[16];
+                if (PRE) {
+#pragma unroll
+                    for (int e = 0; e < 16; e++) f[e] = fw[PRE ? j : 0][e];
                 } else {
-                    const float *xt = xs + t * k;
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const float4 v = *reinterpret_cast<const float4 *>(xt + e8_piece(c, i));
-                        xv[4 * i + 0] = v.x;
-                        xv[4 * i + 1] = v.y;
-                        xv[4 * i + 2] = v.z;
-                        xv[4 * i + 3] = v.w;
-                    }
+                    // decoded per token pair: the empty asm keeps the compiler
+                    // from hoisting all slots' decodes out of the token loop
+                    u32x4 bj = buf[j];
+                    asm volatile("" : "+v"(bj));
+                    e8_decode16(bj, f);
                 }
 #pragma unroll
-                for (int e = 0; e < 16; e++) acc[t] = __builtin_fmaf(xv[e], f[e], acc[t]);
+                for (int e = 0; e < 16; e++) {
+                    a0[j] = __builtin_fmaf(v0[j & 1][e], f[e], a0[j]);
+                    a1[j] = __builtin_fmaf(v1[j & 1][e], f[e], a1[j]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-        }
-        const int row = (wid + nwaves * q) * g.G + gr;
-#pragma unroll
-        for (int t = 0; t < TG; t++) {
-            if (!XREG && t >= tcount) break;
-            float v = acc[t];
-            v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-            v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-            v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-            v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
-            if (g.L >= 32) v = swap16_sum(v);
-            if (g.L >= 64) v = swap32_sum(v);
-            if (li == 0 && row < n) y[(int64_t)(t0 + t) * n + row] = w_scale * v;
+            finish(e8_tree<JM>(a0), t, row, true);
+            finish(e8_tree<JM>(a1), t1, row, t + 1 < tcount);
         }
     };
 
@@ -204,7 +271,7 @@ __global__ __launch_bounds__(kE8Threads) void e4m3_gemv_kernel(const uint8_t *__
     if (!XREG) {
         // stage the group's tokens (after the first tiles are in flight)
         const int quads = tcount * k / 4;
-        for (int p = threadIdx.x; p < quads; p += kE8Threads) {
+        for (int p = threadIdx.x; p < quads; p += NT) {
             const int t = p / (k / 4);
             const int r = p - t * (k / 4);
             const int c = r >> 2, i = r & 3;
@@ -223,7 +290,129 @@ __global__ __launch_bounds__(kE8Threads) void e4m3_gemv_kernel(const uint8_t *__
     }
 }
 
-static bool e8_geom(int m, int k, int n, E8Geom &g) {
+// Verify batches at K > 1024 (two or more chunk slots per lane).  The staged-
+// token kernel above reads 64 bytes of activations from LDS for every 16 fma,
+// which made the LDS as busy as the VALU.  Here the row's chunk slots are
+// spread over the waves of a workgroup: wave j owns slot j (chunk li + 64*j of
+// every row), so a lane needs only its one chunk of each token, 16*MT floats,
+// held in registers for the whole launch.  A workgroup streams items of JP
+// rows; wave j loads slot j of all JP rows (1 KiB per row, one load
+// instruction), computes each token's slot leaf, and parks it in LDS; after
+// one barrier wave r sums row r of the item: the slot tree, then the lane
+// butterfly, the same operations in the same order as the one-token kernel.
+// JP: chunk slots per lane rounded up to a power of two (waves per workgroup,
+// rows per item); MT: token capacity.
+template <int JP, int MT>
+__global__ __launch_bounds__(64 * JP) void e4m3_gemv_slots_kernel(const uint8_t *__restrict__ w,
+                                                                  const float *__restrict__ x, float w_scale,
+                                                                  float *__restrict__ y, int m, int k, int n,
+                                                                  E8Geom g) {
+    constexpr int R = JP;                       // rows per item
+    constexpr int EX = R * MT * JP * 64;        // floats of one exchange buffer
+    extern __shared__ __attribute__((aligned(16))) float ex[];   // [2][R][MT][JP][64]
+    const int lane = threadIdx.x & 63;
+    const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int tg, rwg;
+    if (g.xcd_map) {
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        tg = slot % g.ngroups;
+        rwg = (slot / g.ngroups) * 8 + xcd;
+    } else {
+        tg = blockIdx.x % g.ngroups;
+        rwg = blockIdx.x / g.ngroups;
+    }
+    const int t0 = tg * g.tgsz;
+    const int tcount = min(g.tgsz, m - t0);
+    const int nrwg = gridDim.x / g.ngroups;
+    const int n_items = (n + R - 1) / R;
+    const int Q = rwg < n_items ? (n_items - 1 - rwg) / nrwg + 1 : 0;
+
+    const int c = lane + 64 * j;
+    const bool valid = c < g.CPR;
+    uint32_t off[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) off[r] = valid ? (uint32_t)(r * k + 16 * c) : 0xFFFFFFF0u;
+
+    // this lane's chunk of every token (zeros past the group or the row)
+    float xr[MT][16];
+    {
+        const __amdgpu_buffer_rsrc_t rx = e8_rsrc(x + (int64_t)t0 * k, (uint32_t)tcount * (uint32_t)k * 4u);
+#pragma unroll
+        for (int t = 0; t < MT; t++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t o = (valid && t < tcount) ? (uint32_t)((t * k + 16 * c) * 4 + 16 * i) : 0xFFFFFFF0u;
+                const v4f v = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0));
+#pragma unroll
+                for (int e = 0; e < 4; e++) xr[t][4 * i + e] = v[e];
+            }
+    }
+    const __amdgpu_buffer_rsrc_t ry = e8_rsrc(y, (uint32_t)m * (uint32_t)n * 4u);
+
+    // item q: rows (rwg + nrwg*q)*R ..+R; past the last item the resource is empty
+    auto issue = [&](u32x4 (&buf)[R], int q) {
+        const int64_t row0 = (int64_t)(rwg + nrwg * q) * R;
+        const int64_t rem = ((int64_t)n - row0) * k;
+        const uint32_t bytes = q >= Q ? 0u : (rem > 0x7FFFFFF0ll ? 0x7FFFFFF0u : (uint32_t)rem);
+        const uint8_t *base = q >= Q ? w : w + row0 * k;
+        const __amdgpu_buffer_rsrc_t rs = e8_rsrc(base, bytes);
+#pragma unroll
+        for (int r = 0; r < R; r++)
+            buf[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[r], 0, 2));
+    };
+
+    auto step = [&](const u32x4 (&buf)[R], int q) {
+        float *e = ex + (q & 1) * EX;
+        // slot leaves: one 16-fma chain per row and token, from +0
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            float f[16];
+            e8_decode16(buf[r], f);
+#pragma unroll
+            for (int t = 0; t < MT; t++) {
+                if (t >= tcount) break;
+                float lf = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; i++) lf = __builtin_fmaf(xr[t][i], f[i], lf);
+                e[((r * MT + t) * JP + j) * 64 + lane] = lf;
+            }
+        }
+        __syncthreads();
+        // wave j finishes row j of the item for every token; exactly one
+        // store per token slot (out-of-range offsets for the rest), so the
+        // compiler's waits before the next item stay exact
+        const int64_t row = (int64_t)(rwg + nrwg * q) * R + j;
+#pragma unroll
+        for (int t = 0; t < MT; t++) {
+            float v = 0.0f;
+            if (t < tcount) {
+                const float *sp = e + (j * MT + t) * JP * 64 + lane;
+                float lv[JP];
+#pragma unroll
+                for (int jj = 0; jj < JP; jj++) lv[jj] = sp[jj * 64];
+                v = w_scale * e8_row_sum(e8_tree<JP>(lv), 64);
+            }
+            const uint32_t o = (lane == 0 && t < tcount && row < n) ? (uint32_t)(((int64_t)(t0 + t) * n + row) * 4)
+                                                                  : 0xFFFFFFF0u;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, o, 0, 0);
+        }
+    };
+
+    u32x4 bA[R], bB[R], bC[R];
+    issue(bA, 0);
+    issue(bB, 1);
+    issue(bC, 2);
+    for (int q = 0; q < Q; q += 3) {
+        step(bA, q);
+        issue(bA, q + 3);
+        if (q + 1 < Q) step(bB, q + 1);
+        issue(bB, q + 4);
+        if (q + 2 < Q) step(bC, q + 2);
+        issue(bC, q + 5);
+    }
+}
+
+static bool e8_geom(int m, int k, int n, int tgsz, E8Geom &g) {
     g.CPR = k / 16;
     int L = 16;
     while (L < g.CPR && L < 64) L *= 2;
@@ -232,32 +421,35 @@ static bool e8_geom(int m, int k, int n, E8Geom &g) {
     g.G = 64 / L;
     g.J = (g.CPR + L - 1) / L;
     g.n_items = (n + g.G - 1) / g.G;
-    g.ngroups = (m + kE8MaxTG - 1) / kE8MaxTG;
+    g.tgsz = tgsz;
+    g.ngroups = (m + tgsz - 1) / tgsz;
     return g.J <= 8;
 }
 
-template <int TG, int JM, bool XREG>
+template <int JM, bool XREG, int NT>
 static int e8_launch(const uint8_t *w, const float *x, float w_scale, float *y, int m, int k, int n,
                      const E8Geom &g, hipStream_t stream) {
-    const int lds = XREG ? 0 : TG * k * 4;
+    const int lds = XREG ? 0 : g.tgsz * k * 4;
     static int attr_done = 0;
     if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&e4m3_gemv_kernel<TG, JM, XREG>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&e4m3_gemv_kernel<JM, XREG, NT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kE8LdsBytes);
         if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
         attr_done = 1;
     }
     const int cus = device_cus();
     // resident workgroups per CU (registers and LDS), at most 4
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&e4m3_gemv_kernel<TG, JM, XREG>),
-                                                     kE8Threads, lds) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&e4m3_gemv_kernel<JM, XREG, NT>),
+                                                     NT, lds) != hipSuccess || per_cu < 1)
         per_cu = 1;
     if (per_cu > 4) per_cu = 4;
     // Workgroups per token group: no more than fit at once, and few enough
-    // that each wave has at least four items (each wave also reads the
-    // activations once, which small n would otherwise multiply).
-    int rwgs = (g.n_items + 4 * kE8Waves - 1) / (4 * kE8Waves);
+    // that each wave has at least four items (two in the large workgroups,
+    // whose staged tokens are shared by 8 or 16 waves).
+    const int waves = NT / 64;
+    const int min_items = NT > kE8Threads ? 2 : 4;
+    int rwgs = (g.n_items + min_items * waves - 1) / (min_items * waves);
     int cap = cus * per_cu / g.ngroups;
     if (cap < 1) cap = 1;
     if (rwgs > cap) rwgs = cap;
@@ -268,8 +460,44 @@ static int e8_launch(const uint8_t *w, const float *x, float w_scale, float *y, 
         rwgs -= rwgs % 8;   // every XCD holds whole sets of token groups
         gg.xcd_map = 1;
     }
-    hipLaunchKernelGGL((e4m3_gemv_kernel<TG, JM, XREG>), dim3(rwgs * g.ngroups), dim3(kE8Threads), lds, stream, w, x,
+    hipLaunchKernelGGL((e4m3_gemv_kernel<JM, XREG, NT>), dim3(rwgs * g.ngroups), dim3(NT), lds, stream, w, x,
                        w_scale, y, m, k, n, gg);
+    return launch_status();
+}
+
+template <int JP, int MT>
+static int e8_launch_slots(const uint8_t *w, const float *x, float w_scale, float *y, int m, int k, int n,
+                           const E8Geom &g, hipStream_t stream) {
+    constexpr int NT = 64 * JP;
+    const int lds = 2 * JP * MT * JP * 64 * 4;
+    static int attr_done = 0;
+    if (!attr_done) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&e4m3_gemv_slots_kernel<JP, MT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kE8LdsBytes);
+        if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
+        attr_done = 1;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&e4m3_gemv_slots_kernel<JP, MT>),
+                                                     NT, lds) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    if (per_cu > 4) per_cu = 4;
+    // row workgroups per token group: all that fit at once, but at least 4
+    // items each (every workgroup also loads the group's activations once)
+    const int n_items = (n + JP - 1) / JP;
+    int rwgs = (n_items + 3) / 4;
+    int cap = device_cus() * per_cu / g.ngroups;
+    if (cap < 1) cap = 1;
+    if (rwgs > cap) rwgs = cap;
+    if (rwgs < 1) rwgs = 1;
+    E8Geom gg = g;
+    gg.xcd_map = 0;
+    if (g.ngroups > 1 && rwgs >= 8) {
+        rwgs -= rwgs % 8;
+        gg.xcd_map = 1;
+    }
+    hipLaunchKernelGGL((e4m3_gemv_slots_kernel<JP, MT>), dim3(rwgs * g.ngroups), dim3(NT), lds, stream, w, x, w_scale,
+                       y, m, k, n, gg);
     return launch_status();
 }
 
@@ -284,15 +512,34 @@ extern "C" int bqm_e4m3_gemv(const uint8_t *w, const float *x, float w_scale, fl
     if (k % 256 != 0 || k > kE8MaxK) return BQM_EUNSUPPORTED;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return BQM_EUNSUPPORTED;
     if ((int64_t)n * k > 0x7FFFFFFFll * 64) return BQM_EUNSUPPORTED;
-    E8Geom g;
-    if (!e8_geom(m, k, n, g)) return BQM_EUNSUPPORTED;
     hipStream_t s = as_stream(stream);
-    if (m == 1 && g.J <= 4) return e8_launch<1, 4, true>(w, x, w_scale, y, m, k, n, g, s);
-    if (g.J <= 4) {
-        if (m <= 2) return e8_launch<2, 4, false>(w, x, w_scale, y, m, k, n, g, s);
-        return e8_launch<4, 4, false>(w, x, w_scale, y, m, k, n, g, s);
+    E8Geom g;
+    if (!e8_geom(m, k, n, m, g)) return BQM_EUNSUPPORTED;
+    if (m >= kE8SlotsMinM && g.J >= 2 && (int64_t)m * n * 4 <= 0x7FFFFFF0ll) {
+        // chunk slots spread over the waves of a workgroup, tokens in registers
+        // token capacity: 8 (4 with 8 slots), 10 for 9..10 tokens at 3..4
+        // slots, which then run as one group instead of two (measured: m=9
+        // on 4096->64448 125 us against 139; the larger capacity costs
+        // occupancy and idle token slots elsewhere)
+        const int JP = g.J <= 2 ? 2 : g.J <= 4 ? 4 : 8;
+        const int MT = JP == 8 ? 4 : (JP == 4 && m > 8 && m <= 10) ? 10 : 8;
+        const int ng = (m + MT - 1) / MT;
+        g.tgsz = (m + ng - 1) / ng;
+        g.ngroups = ng;
+        if (JP == 2) return e8_launch_slots<2, 8>(w, x, w_scale, y, m, k, n, g, s);
+        if (JP == 4 && MT == 10) return e8_launch_slots<4, 10>(w, x, w_scale, y, m, k, n, g, s);
+        if (JP == 4) return e8_launch_slots<4, 8>(w, x, w_scale, y, m, k, n, g, s);
+        return e8_launch_slots<8, 4>(w, x, w_scale, y, m, k, n, g, s);
     }
-    if (m == 1) return e8_launch<1, 8, false>(w, x, w_scale, y, m, k, n, g, s);
-    if (m <= 2) return e8_launch<2, 8, false>(w, x, w_scale, y, m, k, n, g, s);
-    return e8_launch<4, 8, false>(w, x, w_scale, y, m, k, n, g, s);
+    if (m <= 2) {
+        if (m == 1 && g.J <= 4) return e8_launch<4, true, kE8Threads>(w, x, w_scale, y, m, k, n, g, s);
+        if (g.J <= 4) return e8_launch<4, false, kE8Threads>(w, x, w_scale, y, m, k, n, g, s);
+        return e8_launch<8, false, kE8Threads>(w, x, w_scale, y, m, k, n, g, s);
+    }
+    int fit = kE8LdsBytes / (k * 4);
+    if (fit > 16) fit = 16;
+    const int ngroups = (m + fit - 1) / fit;
+    if (!e8_geom(m, k, n, (m + ngroups - 1) / ngroups, g)) return BQM_EUNSUPPORTED;
+    if (g.J <= 4) return e8_launch<4, false, kE8GroupThreads>(w, x, w_scale, y, m, k, n, g, s);
+    return e8_launch<8, false, kE8Threads>(w, x, w_scale, y, m, k, n, g, s);
 }

@@ -184,7 +184,9 @@ int bqm_e4m3_gemm(const uint8_t *w, const uint8_t *xq, const float *scales, floa
  *   BQM_EINVAL);
  *   k % 256 == 0 and k <= 8192 (else BQM_EUNSUPPORTED).  Codes with magnitude
  *   0x7F are NaN; callers must not pass them.
- * y[t][r] = w_scale * sum_k x[t][k] * dec(w[r][k]), f32 accumulation.
+ * y[t][r] = w_scale * sum_k x[t][k] * dec(w[r][k]), f32 accumulation.  A
+ * token's result does not depend on m or on the other tokens: decode (m = 1)
+ * and a verify batch give the same bits.
  */
 int bqm_e4m3_gemv(const uint8_t *w, const float *x, float w_scale, float *y, int m, int k, int n,
                   void *stream);

@@ -1,9 +1,10 @@
 """GPU parity of the e4m3 decode GEMV against the CPU oracle.
 
-Bar: within 1e-5 * sum|terms| per output (f32 accumulation of at most 128
-fma per lane and a 6-level tree: (128 + 6) * 2^-24 < 8e-6), exactly 0 where
-sum|terms| is 0; every token's result identical whatever m (decode ==
-verify); outputs pre-filled with NaN to prove they are fully overwritten.
+Bar: within 1e-5 * sum|terms| per output (f32 chains of 16 fma, a slot tree
+of at most 3 levels and a 6-level lane tree: (16 + 3 + 6) * 2^-24 < 1.5e-6),
+exactly 0 where sum|terms| is 0; every token's result identical whatever m
+(decode == verify, across the one-token, staged-token and slot-split
+kernels); outputs pre-filled with NaN to prove they are fully overwritten.
 """
 import numpy as np
 import pytest
@@ -99,3 +100,46 @@ def test_e4m3_gemv_full_size_stacked_expert(bqm, m):
     y = run(bqm, codes, x, ws)
     y_ref, T = oracle.e4m3_gemv(codes, x, ws)
     check(y, y_ref, T, f"m={m} 4096->20480")
+
+
+def singles(bqm, codes, x, ws):
+    return np.concatenate([run(bqm, codes, x[t:t + 1], ws) for t in range(x.shape[0])])
+
+
+def assert_bitwise(y, ys, what):
+    diff = y.view(np.uint32) != ys.view(np.uint32)
+    if diff.any():
+        t, r = np.argwhere(diff)[0]
+        raise AssertionError(f"{what}: {diff.sum()} outputs differ from single-token calls, first (token {t}, row {r})")
+
+
+# k -> chunk slots per lane: 1280: 2 (the second partly empty), 2048: 2,
+# 2304: 3 (a fourth, empty slot wave), 4096: 4, 4352: 5 and 8192: 8 (eight
+# slot waves, 4-token groups)
+@pytest.mark.parametrize("k,n", [(1280, 37), (2048, 5), (2304, 130), (4096, 3), (4352, 61), (8192, 9)])
+def test_e4m3_gemv_slot_split_every_token_count(bqm, k, n):
+    # every m = 2..16 bitwise equal to single-token calls (one, two, three and
+    # four token groups; n below and above the rows of one item)
+    rng = np.random.default_rng(31 * k + n)
+    codes, ws = workloads.e4m3_weights(n, k, rng)
+    x = workloads.activations(16, k, rng, outliers=True)
+    ys = singles(bqm, codes, x, ws)
+    y_ref, T = oracle.e4m3_gemv(codes, x, ws)
+    check(ys, y_ref, T, f"single tokens k={k} n={n}")
+    for m in range(2, 17):
+        y = run(bqm, codes, x[:m], ws)
+        assert_bitwise(y, ys[:m], f"m={m} k={k} n={n}")
+
+
+def test_e4m3_gemv_slot_split_groups_on_xcds(bqm):
+    # enough rows that token groups of the same rows are placed on one XCD
+    # (m = 11: two groups of 6 and 5 tokens; m = 16 at k = 8192: four groups)
+    rng = np.random.default_rng(77)
+    for m, k, n in [(11, 4096, 4099), (16, 8192, 2050)]:
+        codes, ws = workloads.e4m3_weights(n, k, rng)
+        x = workloads.activations(m, k, rng)
+        y = run(bqm, codes, x, ws)
+        y_ref, T = oracle.e4m3_gemv(codes, x, ws)
+        check(y, y_ref, T, f"m={m} k={k} n={n}")
+        sel = [0, m // 2, m - 1]
+        assert_bitwise(y[sel], singles(bqm, codes, x[sel], ws), f"m={m} k={k} n={n}")
