@@ -374,27 +374,53 @@ __global__ __launch_bounds__(64 * JP) void e4m3_gemv_slots_kernel(const uint8_t 
                 float lf = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 16; i++) lf = __builtin_fmaf(xr[t][i], f[i], lf);
-                e[((r * MT + t) * JP + j) * 64 + lane] = lf;
+                e[((r * MT + t) * JP + j) * 64 + (lane ^ (4 * (t & 3)))] = lf;
             }
         }
         __syncthreads();
-        // wave j finishes row j of the item for every token; exactly one
-        // store per token slot (out-of-range offsets for the rest), so the
-        // compiler's waits before the next item stay exact
-        const int64_t row = (int64_t)(rwg + nrwg * q) * R + j;
+        // Wave j finishes row j of the item.  Lane l takes token l/4 and the
+        // lanes li = 16*(l%4) .. +15 of the row: for each li the slot tree,
+        // then the tree over its 16 li, then two DPP levels over the token's
+        // 4 lanes: the same perfect tree over li as the butterfly, with no
+        // cross-lane step below 16.  In the exchange buffer lane li of token
+        // t sits at li ^ 4*(t%4), so the 16 lanes of a b128 read phase (4
+        // tokens x 4 lane blocks) hit 16 distinct 4-bank groups.  Exactly one
+        // store per wave and item (out-of-range offsets for the other lanes),
+        // so the compiler's waits before the next item stay exact.
+        {
+            const int64_t row = (int64_t)(rwg + nrwg * q) * R + j;
+            const int tt = lane >> 2, bq = lane & 3;
+            const int tr = tt < MT ? tt : MT - 1;   // lanes past MT repeat a token and store nothing
+            const float *sp = e + (j * MT + tr) * JP * 64;
+            const int sw = 4 * (tr & 3);
+            float cs[4];
 #pragma unroll
-        for (int t = 0; t < MT; t++) {
-            float v = 0.0f;
-            if (t < tcount) {
-                const float *sp = e + (j * MT + t) * JP * 64 + lane;
-                float lv[JP];
+            for (int cq = 0; cq < 4; cq++) {
+                float v[JP][4];
 #pragma unroll
-                for (int jj = 0; jj < JP; jj++) lv[jj] = sp[jj * 64];
-                v = w_scale * e8_row_sum(e8_tree<JP>(lv), 64);
+                for (int jj = 0; jj < JP; jj++) {
+                    const float4 p4 = *reinterpret_cast<const float4 *>(sp + jj * 64 + ((16 * bq + 4 * cq) ^ sw));
+                    v[jj][0] = p4.x;
+                    v[jj][1] = p4.y;
+                    v[jj][2] = p4.z;
+                    v[jj][3] = p4.w;
+                }
+                float lv[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    float sl[JP];
+#pragma unroll
+                    for (int jj = 0; jj < JP; jj++) sl[jj] = v[jj][i];
+                    lv[i] = e8_tree<JP>(sl);
+                }
+                cs[cq] = e8_tree<4>(lv);
             }
-            const uint32_t o = (lane == 0 && t < tcount && row < n) ? (uint32_t)(((int64_t)(t0 + t) * n + row) * 4)
-                                                                  : 0xFFFFFFF0u;
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, o, 0, 0);
+            float sum = e8_tree<4>(cs);
+            sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, false));
+            sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, false));
+            const uint32_t o = (bq == 0 && tt < tcount && row < n) ? (uint32_t)(((int64_t)(t0 + tt) * n + row) * 4)
+                                                                 : 0xFFFFFFF0u;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, w_scale * sum), ry, o, 0, 0);
         }
     };
 
