@@ -23,9 +23,10 @@
 //    fill whole rounds of the CUs (m=512, N=20480: NT=5, 256 tiles).
 //  * Per stage and 32x32 tile a wave runs two v_mfma_scale_f32_32x32x64_f8f6f4
 //    (unit E8M0 scales) into a block partial P started at zero and folds it
-//    at once, acc += P * (xs[t] * g), two VALU ops per output element; one
-//    partial at a time keeps NT=5 within 216 VGPRs, and the fold of one tile
-//    runs under the next tile's MFMAs.  g is one
+//    at once, acc += P * (xs[t] * g), two VALU ops per output element.  Two
+//    partials are live, so tile j+1's MFMAs are issued before tile j is
+//    folded and the fold runs under them (NT=5: 232 VGPRs; with one partial
+//    register set the next MFMAs waited for the fold).  g is one
 //    scalar per 32-column tile (a 32-aligned tile never straddles a 128-row
 //    block of the grid), read with scalar loads one stage ahead; the 128
 //    token scales of the stage go through LDS with the operand tiles.
@@ -237,13 +238,19 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
             sx[4 * i + 3] = q.w;
         }
         const v16f z = {0};
-#pragma unroll
-        for (int j = 0; j < NT; j++) {
+        auto part = [&](int j) {
             const v8i b0 = ld8(pb + j * 32 * kB8RowStride), b1 = ld8(pb + j * 32 * kB8RowStride + 64);
             v16f P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, z, 0, 0, 0, 127, 0, 127);
-            P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, P, 0, 0, 0, 127, 0, 127);
+            return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, P, 0, 0, 0, 127, 0, 127);
+        };
+        v16f Pc = part(0);
 #pragma unroll
-            for (int v = 0; v < 16; v++) acc[j][v] = __builtin_fmaf(P[v], sx[v] * G[j], acc[j][v]);
+        for (int j = 0; j < NT; j++) {
+            v16f Pn = Pc;
+            if (j + 1 < NT) Pn = part(j + 1 < NT ? j + 1 : j);
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[j][v] = __builtin_fmaf(Pc[v], sx[v] * G[j], acc[j][v]);
+            Pc = Pn;
         }
     };
 
