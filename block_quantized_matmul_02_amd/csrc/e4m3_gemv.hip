@@ -378,28 +378,32 @@ __global__ __launch_bounds__(64 * JP) void e4m3_gemv_slots_kernel(const uint8_t 
             }
         }
         __syncthreads();
-        // Wave j finishes row j of the item.  Lane l takes token l/4 and the
-        // lanes li = 16*(l%4) .. +15 of the row: for each li the slot tree,
-        // then the tree over its 16 li, then two DPP levels over the token's
-        // 4 lanes: the same perfect tree over li as the butterfly, with no
-        // cross-lane step below 16.  In the exchange buffer lane li of token
-        // t sits at li ^ 4*(t%4), so the 16 lanes of a b128 read phase (4
-        // tokens x 4 lane blocks) hit 16 distinct 4-bank groups.  Exactly one
-        // store per wave and item (out-of-range offsets for the other lanes),
-        // so the compiler's waits before the next item stay exact.
+        // Wave j finishes row j of the item.  The wave's lanes are split into
+        // TP token slots of LPT = 64/TP lanes; lane l takes token l/LPT and the
+        // 64/LPT consecutive lane leaves li from 64/LPT*(l%LPT) on: for each li
+        // the slot tree, then the tree over its li, then log2(LPT) DPP levels
+        // over the token's lanes (xor 1, xor 2, half-row mirror, row mirror):
+        // the same perfect tree over li as the butterfly.  In the exchange
+        // buffer lane li of token t sits at li ^ 4*(t%4), so the 16 lanes of
+        // a b128 read phase hit 16 distinct 4-bank groups.  Exactly one store
+        // per wave and item (out-of-range offsets for the other lanes), so
+        // the compiler's waits before the next item stay exact.
         {
+            constexpr int TP = MT <= 4 ? 4 : MT <= 8 ? 8 : 16;   // token slots of the sum
+            constexpr int LPT = 64 / TP;                         // lanes per token
+            constexpr int NC = 16 / LPT;                         // groups of 4 li per lane
             const int64_t row = (int64_t)(rwg + nrwg * q) * R + j;
-            const int tt = lane >> 2, bq = lane & 3;
+            const int tt = lane / LPT, bq = lane % LPT;
             const int tr = tt < MT ? tt : MT - 1;   // lanes past MT repeat a token and store nothing
             const float *sp = e + (j * MT + tr) * JP * 64;
             const int sw = 4 * (tr & 3);
-            float cs[4];
+            float cs[NC];
 #pragma unroll
-            for (int cq = 0; cq < 4; cq++) {
+            for (int cq = 0; cq < NC; cq++) {
                 float v[JP][4];
 #pragma unroll
                 for (int jj = 0; jj < JP; jj++) {
-                    const float4 p4 = *reinterpret_cast<const float4 *>(sp + jj * 64 + ((16 * bq + 4 * cq) ^ sw));
+                    const float4 p4 = *reinterpret_cast<const float4 *>(sp + jj * 64 + ((4 * NC * bq + 4 * cq) ^ sw));
                     v[jj][0] = p4.x;
                     v[jj][1] = p4.y;
                     v[jj][2] = p4.z;
@@ -415,9 +419,13 @@ __global__ __launch_bounds__(64 * JP) void e4m3_gemv_slots_kernel(const uint8_t 
                 }
                 cs[cq] = e8_tree<4>(lv);
             }
-            float sum = e8_tree<4>(cs);
+            float sum = e8_tree<NC>(cs);
             sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, false));
             sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF, false));
+            if (LPT >= 8)
+                sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), 0x141, 0xF, 0xF, false));
+            if (LPT >= 16)
+                sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sum), 0x140, 0xF, 0xF, false));
             const uint32_t o = (bq == 0 && tt < tcount && row < n) ? (uint32_t)(((int64_t)(t0 + tt) * n + row) * 4)
                                                                  : 0xFFFFFFF0u;
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, w_scale * sum), ry, o, 0, 0);
@@ -543,16 +551,18 @@ extern "C" int bqm_e4m3_gemv(const uint8_t *w, const float *x, float w_scale, fl
     if (!e8_geom(m, k, n, m, g)) return BQM_EUNSUPPORTED;
     if (m >= kE8SlotsMinM && g.J >= 2 && (int64_t)m * n * 4 <= 0x7FFFFFF0ll) {
         // chunk slots spread over the waves of a workgroup, tokens in registers
-        // token capacity: 8 (4 with 8 slots), 10 for 9..10 tokens at 3..4
-        // slots, which then run as one group instead of two (measured: m=9
-        // on 4096->64448 125 us against 139; the larger capacity costs
-        // occupancy and idle token slots elsewhere)
+        // token capacity: 4 up to 4 tokens (and always with 8 slots), 10 for
+        // 9..10 tokens at 3..4 slots, which then run as one group instead of
+        // two, else 8 (the larger capacities cost registers, so occupancy,
+        // and idle token slots)
         const int JP = g.J <= 2 ? 2 : g.J <= 4 ? 4 : 8;
-        const int MT = JP == 8 ? 4 : (JP == 4 && m > 8 && m <= 10) ? 10 : 8;
+        const int MT = JP == 8 ? 4 : (JP == 4 && m > 8 && m <= 10) ? 10 : (m <= 4 ? 4 : 8);
         const int ng = (m + MT - 1) / MT;
         g.tgsz = (m + ng - 1) / ng;
         g.ngroups = ng;
+        if (JP == 2 && MT == 4) return e8_launch_slots<2, 4>(w, x, w_scale, y, m, k, n, g, s);
         if (JP == 2) return e8_launch_slots<2, 8>(w, x, w_scale, y, m, k, n, g, s);
+        if (JP == 4 && MT == 4) return e8_launch_slots<4, 4>(w, x, w_scale, y, m, k, n, g, s);
         if (JP == 4 && MT == 10) return e8_launch_slots<4, 10>(w, x, w_scale, y, m, k, n, g, s);
         if (JP == 4) return e8_launch_slots<4, 8>(w, x, w_scale, y, m, k, n, g, s);
         return e8_launch_slots<8, 4>(w, x, w_scale, y, m, k, n, g, s);
