@@ -551,15 +551,20 @@ extern "C" int bqm_e4m3_gemv(const uint8_t *w, const float *x, float w_scale, fl
     if (!e8_geom(m, k, n, m, g)) return BQM_EUNSUPPORTED;
     if (m >= kE8SlotsMinM && g.J >= 2 && (int64_t)m * n * 4 <= 0x7FFFFFF0ll) {
         // chunk slots spread over the waves of a workgroup, tokens in registers
-        // token capacity: 4 up to 4 tokens (and always with 8 slots), 10 for
-        // 9..10 tokens at 3..4 slots, which then run as one group instead of
-        // two, else 8 (the larger capacities cost registers, so occupancy,
-        // and idle token slots)
+        // token capacity: 2 for two tokens, 4 up to 4 tokens (and always with
+        // 8 slots), 10 for 9..10 tokens at 3..4 slots, which then run as one
+        // group instead of two, else 8 (the larger capacities cost registers,
+        // so occupancy, and idle token slots)
         const int JP = g.J <= 2 ? 2 : g.J <= 4 ? 4 : 8;
-        const int MT = JP == 8 ? 4 : (JP == 4 && m > 8 && m <= 10) ? 10 : (m <= 4 ? 4 : 8);
+        const int MT = m <= 2 ? 2 : JP == 8 ? 4 : (JP == 4 && m > 8 && m <= 10) ? 10 : (m <= 4 ? 4 : 8);
         const int ng = (m + MT - 1) / MT;
         g.tgsz = (m + ng - 1) / ng;
         g.ngroups = ng;
+        if (MT == 2) {
+            if (JP == 2) return e8_launch_slots<2, 2>(w, x, w_scale, y, m, k, n, g, s);
+            if (JP == 4) return e8_launch_slots<4, 2>(w, x, w_scale, y, m, k, n, g, s);
+            return e8_launch_slots<8, 2>(w, x, w_scale, y, m, k, n, g, s);
+        }
         if (JP == 2 && MT == 4) return e8_launch_slots<2, 4>(w, x, w_scale, y, m, k, n, g, s);
         if (JP == 2) return e8_launch_slots<2, 8>(w, x, w_scale, y, m, k, n, g, s);
         if (JP == 4 && MT == 4) return e8_launch_slots<4, 4>(w, x, w_scale, y, m, k, n, g, s);
