@@ -19,14 +19,14 @@
 //
 // The GEMM uses v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales
 // (E8M0 127 = 2^0): 32x32 outputs per 64-deep step, f32 accumulation, the
-// folded scale applied once in the epilogue.  Workgroup tile 128 x 64*NT
-// (4 waves of 64 x 32*NT, NT = 2..5 chosen per shape so the tiles spread
-// evenly over the CUs: m=512, N=20480 takes NT=5, 256 tiles of 128 x 320,
-// one per CU); k staged 128 at a time in double-buffered LDS with padded
-// 144-byte rows (conflict-free reads, immediate offsets), global loads one
-// stage ahead in registers, operand reads for the next 64-deep step slotted
-// between the current step's MFMAs.  Accumulators live in AGPRs (up to 160
-// per lane), leaving the VGPRs to the operand and load pipelines.
+// folded scale applied once in the epilogue.
+// Workgroup tile 128 x 64*NT (8 waves in 4 x 2, each 32 x 32*NT, two per
+// SIMD; NT = 2..5 chosen per shape so the tiles spread evenly over the CUs:
+// m=512, N=20480 takes NT=5, 256 tiles of 128 x 320, one per CU); k staged
+// 128 at a time in double-buffered LDS with padded 144-byte rows
+// (conflict-free reads, immediate offsets), global loads two stages ahead
+// in registers, operand reads for the next 64-deep step slotted between the
+// current step's MFMAs.
 #include "bqmm_internal.h"
 
 namespace bqm {
