@@ -231,8 +231,12 @@ def sample_pairs(m, n, rng, count=2048):
     return np.concatenate([tok, corners_t]), np.concatenate([row, corners_r])
 
 
-@pytest.mark.parametrize("m,k,n", [(1, 4096, 4096), (1, 4096, 64448), (9, 4096, 20480), (1, 1280, 4096),
-                                   (9, 4096, 5152)])
+# the decode head (m=1) and all eight decode/verify sweep cases (m = 1 and 9
+# over 4096->5152, 4096->4096, 1280->4096, 4096->20480), at full size, on
+# sampled outputs
+@pytest.mark.parametrize("m,k,n", [(1, 4096, 4096), (1, 4096, 64448), (1, 4096, 5152), (1, 4096, 20480),
+                                   (1, 1280, 4096), (9, 4096, 4096), (9, 4096, 5152), (9, 4096, 20480),
+                                   (9, 1280, 4096)])
 def test_gemv_full_size_workloads(bqm, m, k, n):
     rng = np.random.default_rng(0)
     w = workloads.q8_0_weights(n, k, rng)
