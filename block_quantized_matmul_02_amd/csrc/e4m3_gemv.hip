@@ -48,8 +48,8 @@ namespace bqm {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kE8Threads = 256;       // workgroup for one and two tokens
-constexpr int kE8GroupThreads = 512;  // workgroup for three or more tokens
+constexpr int kE8Threads = 256;       // workgroup of the one-token kernel and of staged tokens up to 2
+constexpr int kE8GroupThreads = 512;  // staged-token workgroup for three or more tokens
 constexpr int kE8SlotsMinM = 2;       // fewest tokens for the slot-split kernel
 constexpr int kE8MaxK = 8192;
 constexpr int kE8LdsBytes = 160 * 1024;
