@@ -200,82 +200,100 @@ __global__ __launch_bounds__(kF8Threads) void e4m3_gemm_kernel(const uint8_t *__
     const int khalf = lane >> 5;
     // Lane l supplies row l%32 of each 32-row operand tile and k values
     // 32*(l/32) .. +31 of the 64-deep step (the same k set for A and B).
-    auto compute_stage = [&](const F8Stage<NT> &S) {
-        const uint8_t *pa = S.a + (wm * 32 + (lane & 31)) * kF8RowStride + 32 * khalf;
-        const uint8_t *pb = S.b + (wn * 32 * NT + (lane & 31)) * kF8RowStride + 32 * khalf;
-        v8i a[2], b[2][NT];   // [k-step parity][tile]
-        auto ld8 = [](const uint8_t *p) {
-            const u32x4 lo = *reinterpret_cast<const u32x4 *>(p);
-            const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + 16);
-            return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        };
-        auto rd = [&](int ks, int slot) {
-            a[slot] = ld8(pa + 64 * ks);
+    // Operands of a 64-deep step live in slot 0 (step 0 of a stage) or slot 1
+    // (step 1), kept across stages.
+    v8i a[2], b[2][NT];
+    auto ld8 = [](const uint8_t *p) {
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(p);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(p + 16);
+        return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    auto rd = [&](const F8Stage<NT> &S, int ks, int slot) {
+        const uint8_t *pa = S.a + (wm * 32 + (lane & 31)) * kF8RowStride + 32 * khalf + 64 * ks;
+        const uint8_t *pb = S.b + (wn * 32 * NT + (lane & 31)) * kF8RowStride + 32 * khalf + 64 * ks;
+        a[slot] = ld8(pa);
 #pragma unroll
-            for (int j = 0; j < NT; j++) b[slot][j] = ld8(pb + j * 32 * kF8RowStride + 64 * ks);
-        };
-        rd(0, 0);
+        for (int j = 0; j < NT; j++) b[slot][j] = ld8(pb + j * 32 * kF8RowStride);
+    };
+    auto mfma_step = [&](int slot) {
 #pragma unroll
-        for (int ks = 0; ks < kF8KB / 64; ks++) {
-            if (ks + 1 < kF8KB / 64) rd(ks + 1, (ks + 1) & 1);
+        for (int j = 0; j < NT; j++)
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[slot], b[slot][j], acc[j], 0, 0, 0, 127, 0,
+                                                                   127);
+    };
+    // Scheduling groups (masks: 0x020 VMEM read, 0x100 DS read, 0x200 DS
+    // write, 0x008 MFMA).  Before the barrier: the global loads, then step
+    // 0's MFMAs one at a time with step 1's operand reads and the next
+    // stage's stores between them.  After it: step 1's MFMAs with the next
+    // stage's step-0 operand reads between them.
+    auto groups_before = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 + NT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-            for (int j = 0; j < NT; j++)
-                acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks & 1], b[ks & 1][j], acc[j], 0, 0, 0, 127,
-                                                                       0, 127);
+        for (int r = 0; r < NT; r++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+    };
+    auto groups_after = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int r = 0; r < NT; r++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        // end of the scheduling region: nothing of the next stage moves up
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // Two register copies: the loads of stage kc+2 are issued while stage kc
     // is computed, and written to LDS one stage later.  Past the last stage
     // the loads re-read it (unconditional loads keep the compiler's count of
-    // loads in flight exact).  Each half-iteration is one basic block for the
-    // scheduling groups: global loads first, then the operand reads of the
-    // first 64-deep step, then the MFMAs one at a time with the second step's
-    // operand reads and then the stage stores slotted between them.  Masks:
-    // 0x020 VMEM read, 0x100 DS read, 0x200 DS write, 0x008 MFMA.
+    // loads in flight exact).  The barrier sits between a stage's two 64-deep
+    // steps: once the next stage's stores are complete, its step-0 operands
+    // are read while this stage's step-1 MFMAs run, so no stage starts by
+    // waiting for its own LDS reads.  (__syncthreads waits for this wave's
+    // LDS reads too, so a buffer is fully consumed before it is rewritten one
+    // stage later.)
     F8Regs<NT> R0, R1;
     const int last = nstage - 1;
     load_stage(R0, 0);
     load_stage(R1, min(1, last));
     store_stage(st[0], R0);
     __syncthreads();
+    rd(st[0], 0, 0);
     int kc = 0;
 #pragma unroll 1
     for (; kc + 1 < nstage; kc += 2) {
+        // stage kc in st[0]; R1 holds stage kc+1
         load_stage(R0, min(kc + 2, last));
-        compute_stage(st[0]);
+        rd(st[0], 1, 1);
+        mfma_step(0);
         store_stage(st[1], R1);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2 + NT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * NT, 0);
-#pragma unroll
-        for (int r = 0; r < NT; r++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < NT; r++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        }
+        groups_before();
         __syncthreads();
+        rd(st[1], 0, 0);
+        mfma_step(1);
+        groups_after();
+        // stage kc+1 in st[1]; R0 holds stage kc+2
         load_stage(R1, min(kc + 3, last));
-        compute_stage(st[1]);
+        rd(st[1], 1, 1);
+        mfma_step(0);
         store_stage(st[0], R0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2 + NT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * NT, 0);
-#pragma unroll
-        for (int r = 0; r < NT; r++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < NT; r++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        }
+        groups_before();
         __syncthreads();
+        rd(st[0], 0, 0);
+        mfma_step(1);
+        groups_after();
     }
-    if (kc < nstage) compute_stage(st[0]);
+    if (kc < nstage) {
+        // an odd last stage, in st[0], its step-0 operands already read
+        rd(st[0], 1, 1);
+        mfma_step(0);
+        mfma_step(1);
+    }
 
     const float sc = scales[2];
 #pragma unroll
