@@ -156,23 +156,61 @@ __global__ __launch_bounds__(kH16Threads) void f16_gemm_kernel(const uint16_t *_
 
     const int khalf = lane >> 5;
     constexpr int kSteps = kH16KB / 32;   // 16 fp16 values (32 bytes) per MFMA step
-    auto compute_stage = [&](const H16Stage<NT> &S) {
-        const uint8_t *pa = S.a + (wm * 32 + (lane & 31)) * kH16RowStride + 16 * khalf;
-        const uint8_t *pb = S.b + (wn * 32 * NT + (lane & 31)) * kH16RowStride + 16 * khalf;
-        v8h a[2], b[2][NT];   // [step parity][tile]
-        auto rd = [&](int ks, int slot) {
-            a[slot] = *reinterpret_cast<const v8h *>(pa + 32 * ks);
+    static_assert(kSteps % 2 == 0, "operand slots alternate by step parity across stages");
+    // Operands of a 16-deep step in slot (step parity), kept across stages.
+    v8h a[2], b[2][NT];
+    auto rd = [&](const H16Stage<NT> &S, int ks, int slot) {
+        const uint8_t *pa = S.a + (wm * 32 + (lane & 31)) * kH16RowStride + 16 * khalf + 32 * ks;
+        const uint8_t *pb = S.b + (wn * 32 * NT + (lane & 31)) * kH16RowStride + 16 * khalf + 32 * ks;
+        a[slot] = *reinterpret_cast<const v8h *>(pa);
 #pragma unroll
-            for (int j = 0; j < NT; j++) b[slot][j] = *reinterpret_cast<const v8h *>(pb + j * 32 * kH16RowStride + 32 * ks);
-        };
-        rd(0, 0);
+        for (int j = 0; j < NT; j++) b[slot][j] = *reinterpret_cast<const v8h *>(pb + j * 32 * kH16RowStride);
+    };
+    auto mfma_step = [&](int slot) {
 #pragma unroll
-        for (int ks = 0; ks < kSteps; ks++) {
-            if (ks + 1 < kSteps) rd(ks + 1, (ks + 1) & 1);
+        for (int j = 0; j < NT; j++)
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[slot], b[slot][j], acc[j], 0, 0, 0);
+    };
+    // One stage: steps 0 .. kSteps-2 with the next step's operand reads under
+    // their MFMAs and the next stage's stores after them; then the barrier;
+    // then the last step's MFMAs with the next stage's step-0 reads under
+    // them, so no stage starts by waiting for its own LDS reads.  The
+    // scheduling barrier closes the region so the compiler does not pull the
+    // next stage's reads forward.  (__syncthreads waits for this wave's LDS
+    // reads too, so a buffer is fully consumed before it is rewritten one
+    // stage later.)
+    // Scheduling groups (masks: 0x020 VMEM read, 0x100 DS read, 0x200 DS
+    // write, 0x008 MFMA): the stage's global loads, then per step one operand
+    // read and NT x (one MFMA, one read), then the stores; after the barrier
+    // the same pattern for the last step.
+    auto stage_body = [&](const H16Stage<NT> &cur, H16Stage<NT> &nxt, const H16Regs<NT> &Rn, bool store) {
 #pragma unroll
-            for (int j = 0; j < NT; j++)
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks & 1], b[ks & 1][j], acc[j], 0, 0, 0);
+        for (int ks = 0; ks + 1 < kSteps; ks++) {
+            rd(cur, ks + 1, (ks + 1) & 1);
+            mfma_step(ks & 1);
         }
+        if (store) store_stage(nxt, Rn);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 + NT, 0);
+#pragma unroll
+        for (int ks = 0; ks + 1 < kSteps; ks++) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+            for (int j = 0; j < NT; j++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 2 + NT, 0);
+        __syncthreads();
+        rd(nxt, 0, 0);
+        mfma_step((kSteps - 1) & 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int j = 0; j < NT; j++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // Two register copies: the loads of stage kc+2 are issued while stage kc
@@ -185,19 +223,24 @@ __global__ __launch_bounds__(kH16Threads) void f16_gemm_kernel(const uint16_t *_
     load_stage(R1, min(1, last));
     store_stage(st[0], R0);
     __syncthreads();
+    rd(st[0], 0, 0);
     int kc = 0;
 #pragma unroll 1
     for (; kc + 1 < nstage; kc += 2) {
         load_stage(R0, min(kc + 2, last));
-        compute_stage(st[0]);
-        store_stage(st[1], R1);
-        __syncthreads();
+        stage_body(st[0], st[1], R1, true);    // stage kc; stores stage kc+1
         load_stage(R1, min(kc + 3, last));
-        compute_stage(st[1]);
-        store_stage(st[0], R0);
-        __syncthreads();
+        stage_body(st[1], st[0], R0, true);    // stage kc+1; stores stage kc+2 (the last again past the end)
     }
-    if (kc < nstage) compute_stage(st[0]);
+    if (kc < nstage) {
+        // an odd last stage, in st[0], its step-0 operands already read
+#pragma unroll
+        for (int ks = 0; ks + 1 < kSteps; ks++) {
+            rd(st[0], ks + 1, (ks + 1) & 1);
+            mfma_step(ks & 1);
+        }
+        mfma_step((kSteps - 1) & 1);
+    }
 
 #pragma unroll
     for (int j = 0; j < NT; j++) {
