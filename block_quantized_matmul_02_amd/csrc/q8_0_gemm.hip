@@ -219,42 +219,52 @@ __global__ __launch_bounds__(4 * BM) void q8_0_gemm_kernel(const uint8_t *__rest
 #pragma unroll
     for (int v = 0; v < 16; v++) acc[v] = 0.0f;
 
-    const int arow = wm * 32 + (lane & 31);   // A operand row (token) of this lane
-    const int brow = wn * 32 + (lane & 31);   // B operand row (weight row) of this lane
-    const int khalf = lane >> 5;
+    // EARLY (the int8 128-row tile) moves the workgroup barrier into the
+    // stage (below; measured N=4096 37.6 -> 35.5 us, N=20480 164.8 -> 162.0
+    // us, bitwise the same).  The 64-row tile and the fp8 accumulator arm keep
+    // the barrier after the stage: the state the early barrier keeps live
+    // across it does not fit their registers (257 VGPRs or scratch).
+    constexpr bool EARLY = BM == 128 && !F8ACC;
+    if constexpr (EARLY) {
+        const int arow = wm * 32 + (lane & 31);   // A operand row (token) of this lane
+        const int brow = wn * 32 + (lane & 31);   // B operand row (weight row) of this lane
+        const int khalf = lane >> 5;
 
-    // One stage: 8 blocks.  Quant operands are read two blocks ahead and the
-    // int8 MFMA runs one block ahead of the fold.  The scale products
-    // d_x[t][b] * d_w[r][b] come from the matrix core as well: one
-    // v_mfma_f32_32x32x1_2b_f32 forms the 32x32 outer products of two blocks
-    // (lanes 0-31 carry block b, lanes 32-63 block b+1; each result element
-    // is one correctly rounded f32 product, as a VALU multiply would give),
-    // in the same register layout as the int32 block sums.  That leaves two
-    // VALU ops per output and block: convert S, then fma into the
-    // accumulator.  The outer products of a pair are issued one pair ahead.
-    auto compute_stage = [&](const Stage &S) {
+        // One stage: 8 blocks.  Quant operands are read two blocks ahead and the
+        // int8 MFMA runs one block ahead of the fold.  The scale products
+        // d_x[t][b] * d_w[r][b] come from the matrix core as well: one
+        // v_mfma_f32_32x32x1_2b_f32 forms the 32x32 outer products of two blocks
+        // (lanes 0-31 carry block b, lanes 32-63 block b+1; each result element
+        // is one correctly rounded f32 product, as a VALU multiply would give),
+        // in the same register layout as the int32 block sums.  That leaves two
+        // VALU ops per output and block: convert S, then fma into the
+        // accumulator.  The outer products of a pair are issued one pair ahead.
+        //
+        // The workgroup barrier sits before the fold of blocks 6 and 7: the next
+        // stage's stores are issued before it, and after it the next stage's
+        // scales, first two blocks' operands and first MFMAs are issued under
+        // those two folds, so no stage starts by waiting for its own LDS reads.
+        // The operand slots, scales, partial products and block sums are kept
+        // across stages.
+        using BlockSum = typename std::conditional<F8ACC, v16f, v16i>::type;
         v4i A[3], B[3];
-        const uint8_t *xa = S.x + arow * kMmqRowStride + 16 * khalf;
-        const uint8_t *wb = S.w + brow * kMmqRowStride + 128 * khalf;
-        auto rd = [&](int b, int slot) {
-            A[slot] = *reinterpret_cast<const v4i *>(xa + 32 * b);
-            B[slot] = *reinterpret_cast<const v4i *>(wb + 16 * b);
-        };
-        // scale operands of the 4 block pairs: d_x[b + khalf][token], d_w[b + khalf][weight row]
-        float SA[kMmqBlocks / 2], SB[kMmqBlocks / 2];
-#pragma unroll
-        for (int p = 0; p < kMmqBlocks / 2; p++) {
-            SA[p] = S.dx[2 * p + khalf][arow];
-            SB[p] = S.dw[2 * p + khalf][brow];
-        }
-        const v32f z32 = {0};
+        float SA[kMmqBlocks / 2], SB[kMmqBlocks / 2];   // d_x[b + khalf][token], d_w[b + khalf][weight row] per pair
         v32f P[2];
-        rd(0, 0);
-        rd(1, 1);
-        P[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(SA[0], SB[0], z32, 0, 0, 0);
+        BlockSum Sn;
+        const v32f z32 = {0};
+        auto rd = [&](const Stage &S, int b, int slot) {
+            A[slot] = *reinterpret_cast<const v4i *>(S.x + arow * kMmqRowStride + 16 * khalf + 32 * b);
+            B[slot] = *reinterpret_cast<const v4i *>(S.w + brow * kMmqRowStride + 128 * khalf + 16 * b);
+        };
+        auto read_scales = [&](const Stage &S) {
+    #pragma unroll
+            for (int p = 0; p < kMmqBlocks / 2; p++) {
+                SA[p] = S.dx[2 * p + khalf][arow];
+                SB[p] = S.dw[2 * p + khalf][brow];
+            }
+        };
         // the block sums of one 32x32 tile: int32 from the int8 MFMA, or f32
         // from two fp8 MFMAs over the same bytes
-        using BlockSum = typename std::conditional<F8ACC, v16f, v16i>::type;
         auto block_sum = [&](const v4i &a, const v4i &b) -> BlockSum {
             if constexpr (F8ACC) {
                 typedef long v2l __attribute__((ext_vector_type(2)));
@@ -267,64 +277,201 @@ __global__ __launch_bounds__(4 * BM) void q8_0_gemm_kernel(const uint8_t *__rest
                 return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
             }
         };
-        BlockSum Sn = block_sum(A[0], B[0]);
-#pragma unroll
-        for (int b = 0; b < kMmqBlocks; b++) {
-            if (b + 2 < kMmqBlocks) rd(b + 2, (b + 2) % 3);
+        // the first block's MFMAs and operands of a stage (before its fold loop)
+        auto start_stage = [&](const Stage &S) {
+            read_scales(S);
+            rd(S, 0, 0);
+            rd(S, 1, 1);
+            P[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(SA[0], SB[0], z32, 0, 0, 0);
+            Sn = block_sum(A[0], B[0]);
+        };
+        // block b of stage S; in blocks 6 and 7 the first reads and MFMAs of the
+        // next stage (buffer N) are issued under the fold
+        auto block = [&](const Stage &S, const Stage &N, int b) {
+            if (b + 2 < kMmqBlocks) rd(S, b + 2, (b + 2) % 3);
+            if (b == 6) {
+                read_scales(N);   // pair 3's scale product was issued at block 4
+                rd(N, 0, 0);      // slot 0 was last read by block 6's MFMA (issued at block 5)
+            }
             const BlockSum Sc = Sn;
             if (b + 1 < kMmqBlocks) Sn = block_sum(A[(b + 1) % 3], B[(b + 1) % 3]);
             if ((b & 1) == 0 && b + 2 < kMmqBlocks)
-                P[((b + 2) >> 1) & 1] =
-                    __builtin_amdgcn_mfma_f32_32x32x1f32(SA[(b + 2) >> 1], SB[(b + 2) >> 1], z32, 0, 0, 0);
+                P[((b + 2) >> 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x1f32(SA[(b + 2) >> 1], SB[(b + 2) >> 1], z32, 0, 0, 0);
+            if (b == 7) {
+                rd(N, 1, 1);      // slot 1 was last read by block 7's MFMA (issued at block 6)
+                P[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(SA[0], SB[0], z32, 0, 0, 0);   // P[0] held pair 2
+            }
             // Issue those MFMAs before the fold below (they then run under the
             // fold's VALU work instead of stalling the next block's fold): the
-            // empty asm claims to modify the accumulators, so no fold
-            // instruction can move above it, and it reads Sn, so the block-sum
-            // MFMA cannot move below it.
+            // empty asm claims to modify the accumulators, so no fold instruction
+            // can move above it, and it reads Sn, so the block-sum MFMA cannot
+            // move below it.
             asm volatile("" : "+v"(Sn), "+v"(acc));
             const v32f &Pc = P[(b >> 1) & 1];
             const int h = 16 * (b & 1);
-#pragma unroll
+    #pragma unroll
             for (int v = 0; v < 16; v++) {
                 if constexpr (F8ACC)
                     acc[v] = __builtin_fmaf(Sc[v], Pc[h + v], acc[v]);
                 else
                     acc[v] = __builtin_fmaf((float)Sc[v], Pc[h + v], acc[v]);
             }
-            // Keep each block's group (reads for b+2, MFMAs for b+1, fold of
-            // b) in this order: an empty asm that reads and writes the
-            // accumulators stops the compiler from hoisting every block's loads
-            // and MFMAs to the top (which costs registers and serializes the
-            // fold behind them).  The empty asm emits no instruction.
+            if (b == 7) Sn = block_sum(A[0], B[0]);   // the next stage's block 0
+            // Keep each block's group (reads for b+2, MFMAs for b+1, fold of b) in
+            // this order: an empty asm that reads and writes the accumulators stops
+            // the compiler from hoisting every block's loads and MFMAs to the top
+            // (which costs registers and serializes the fold behind them).  The
+            // empty asm emits no instruction.
             asm volatile("" : "+v"(acc) :: "memory");
-        }
-    };
+        };
+        auto pre = [&](const Stage &S, const Stage &N) {
+    #pragma unroll
+            for (int b = 0; b < kMmqBlocks - 2; b++) block(S, N, b);
+        };
+        auto post = [&](const Stage &S, const Stage &N) {
+            block(S, N, kMmqBlocks - 2);
+            block(S, N, kMmqBlocks - 1);
+        };
 
-    // The loads are unconditional (past the last stage they re-read it, an L2
-    // hit): with a branch around them the compiler cannot count the loads in
-    // flight, and its wait before writing the older register buffer to LDS
-    // would then also wait for the loads just issued.
-    Regs R0, R1;
-    const int last = nstage - 1;
-    load_stage(R0, 0);
-    load_stage(R1, min(1, last));
-    store_stage(st[0], R0);
-    __syncthreads();
-    for (int kc = 0; kc < nstage; kc += 2) {
-        // st[0] holds stage kc; R1 holds stage kc+1 (in flight)
-        load_stage(R0, min(kc + 2, last));
-        compute_stage(st[0]);
-        if (kc + 1 < nstage) store_stage(st[1], R1);
+        // The loads are unconditional (past the last stage they re-read it, an L2
+        // hit): with a branch around them the compiler cannot count the loads in
+        // flight, and its wait before writing the older register buffer to LDS
+        // would then also wait for the loads just issued.  Past the last stage
+        // the next-stage reads of blocks 6 and 7 read a stale buffer; their
+        // results are never folded.
+        Regs R0, R1;
+        const int last = nstage - 1;
+        load_stage(R0, 0);
+        load_stage(R1, min(1, last));
+        store_stage(st[0], R0);
         __syncthreads();
-        if (kc + 1 < nstage) {
-            load_stage(R1, min(kc + 3, last));
-            compute_stage(st[1]);
-            if (kc + 2 < nstage) store_stage(st[0], R0);
+        start_stage(st[0]);
+        for (int kc = 0; kc < nstage; kc += 2) {
+            // st[0] holds stage kc; R1 holds stage kc+1 (in flight)
+            load_stage(R0, min(kc + 2, last));
+            pre(st[0], st[1]);
+            if (kc + 1 < nstage) store_stage(st[1], R1);
             __syncthreads();
+            post(st[0], st[1]);
+            if (kc + 1 < nstage) {
+                load_stage(R1, min(kc + 3, last));
+                pre(st[1], st[0]);
+                if (kc + 2 < nstage) store_stage(st[0], R0);
+                __syncthreads();
+                post(st[1], st[0]);
+            }
         }
+
+    } else {
+        const int arow = wm * 32 + (lane & 31);   // A operand row (token) of this lane
+        const int brow = wn * 32 + (lane & 31);   // B operand row (weight row) of this lane
+        const int khalf = lane >> 5;
+
+        // One stage: 8 blocks.  Quant operands are read two blocks ahead and the
+        // int8 MFMA runs one block ahead of the fold.  The scale products
+        // d_x[t][b] * d_w[r][b] come from the matrix core as well: one
+        // v_mfma_f32_32x32x1_2b_f32 forms the 32x32 outer products of two blocks
+        // (lanes 0-31 carry block b, lanes 32-63 block b+1; each result element
+        // is one correctly rounded f32 product, as a VALU multiply would give),
+        // in the same register layout as the int32 block sums.  That leaves two
+        // VALU ops per output and block: convert S, then fma into the
+        // accumulator.  The outer products of a pair are issued one pair ahead.
+        auto compute_stage = [&](const Stage &S) {
+            v4i A[3], B[3];
+            const uint8_t *xa = S.x + arow * kMmqRowStride + 16 * khalf;
+            const uint8_t *wb = S.w + brow * kMmqRowStride + 128 * khalf;
+            auto rd = [&](int b, int slot) {
+                A[slot] = *reinterpret_cast<const v4i *>(xa + 32 * b);
+                B[slot] = *reinterpret_cast<const v4i *>(wb + 16 * b);
+            };
+            // scale operands of the 4 block pairs: d_x[b + khalf][token], d_w[b + khalf][weight row]
+            float SA[kMmqBlocks / 2], SB[kMmqBlocks / 2];
+    #pragma unroll
+            for (int p = 0; p < kMmqBlocks / 2; p++) {
+                SA[p] = S.dx[2 * p + khalf][arow];
+                SB[p] = S.dw[2 * p + khalf][brow];
+            }
+            const v32f z32 = {0};
+            v32f P[2];
+            rd(0, 0);
+            rd(1, 1);
+            P[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(SA[0], SB[0], z32, 0, 0, 0);
+            // the block sums of one 32x32 tile: int32 from the int8 MFMA, or f32
+            // from two fp8 MFMAs over the same bytes
+            using BlockSum = typename std::conditional<F8ACC, v16f, v16i>::type;
+            auto block_sum = [&](const v4i &a, const v4i &b) -> BlockSum {
+                if constexpr (F8ACC) {
+                    typedef long v2l __attribute__((ext_vector_type(2)));
+                    const v16f zf = {0};
+                    const v2l av = __builtin_bit_cast(v2l, a), bv = __builtin_bit_cast(v2l, b);
+                    const v16f lo = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av[0], bv[0], zf, 0, 0, 0);
+                    return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av[1], bv[1], lo, 0, 0, 0);
+                } else {
+                    const v16i z = {0};
+                    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
+                }
+            };
+            BlockSum Sn = block_sum(A[0], B[0]);
+    #pragma unroll
+            for (int b = 0; b < kMmqBlocks; b++) {
+                if (b + 2 < kMmqBlocks) rd(b + 2, (b + 2) % 3);
+                const BlockSum Sc = Sn;
+                if (b + 1 < kMmqBlocks) Sn = block_sum(A[(b + 1) % 3], B[(b + 1) % 3]);
+                if ((b & 1) == 0 && b + 2 < kMmqBlocks)
+                    P[((b + 2) >> 1) & 1] =
+                        __builtin_amdgcn_mfma_f32_32x32x1f32(SA[(b + 2) >> 1], SB[(b + 2) >> 1], z32, 0, 0, 0);
+                // Issue those MFMAs before the fold below (they then run under the
+                // fold's VALU work instead of stalling the next block's fold): the
+                // empty asm claims to modify the accumulators, so no fold
+                // instruction can move above it, and it reads Sn, so the block-sum
+                // MFMA cannot move below it.
+                asm volatile("" : "+v"(Sn), "+v"(acc));
+                const v32f &Pc = P[(b >> 1) & 1];
+                const int h = 16 * (b & 1);
+    #pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    if constexpr (F8ACC)
+                        acc[v] = __builtin_fmaf(Sc[v], Pc[h + v], acc[v]);
+                    else
+                        acc[v] = __builtin_fmaf((float)Sc[v], Pc[h + v], acc[v]);
+                }
+                // Keep each block's group (reads for b+2, MFMAs for b+1, fold of
+                // b) in this order: an empty asm that reads and writes the
+                // accumulators stops the compiler from hoisting every block's loads
+                // and MFMAs to the top (which costs registers and serializes the
+                // fold behind them).  The empty asm emits no instruction.
+                asm volatile("" : "+v"(acc) :: "memory");
+            }
+        };
+
+        // The loads are unconditional (past the last stage they re-read it, an L2
+        // hit): with a branch around them the compiler cannot count the loads in
+        // flight, and its wait before writing the older register buffer to LDS
+        // would then also wait for the loads just issued.
+        Regs R0, R1;
+        const int last = nstage - 1;
+        load_stage(R0, 0);
+        load_stage(R1, min(1, last));
+        store_stage(st[0], R0);
+        __syncthreads();
+        for (int kc = 0; kc < nstage; kc += 2) {
+            // st[0] holds stage kc; R1 holds stage kc+1 (in flight)
+            load_stage(R0, min(kc + 2, last));
+            compute_stage(st[0]);
+            if (kc + 1 < nstage) store_stage(st[1], R1);
+            __syncthreads();
+            if (kc + 1 < nstage) {
+                load_stage(R1, min(kc + 3, last));
+                compute_stage(st[1]);
+                if (kc + 2 < nstage) store_stage(st[0], R0);
+                __syncthreads();
+            }
+        }
+
     }
 
     // Output element (row 8*(v/4) + 4*khalf + v%4, column lane%32) of the wave tile.
+    const int khalf = lane >> 5;
     const int col = n0 + wn * 32 + (lane & 31);
     if (col < n) {
 #pragma unroll
