@@ -162,8 +162,10 @@ def gemm_case(bqm, m, k, n, seed):
 # the tile widths 2..5 (64*NT output columns per workgroup) are all reached:
 # small shapes take NT=2, (128, 128, 40000) NT=3, (256, 256, 30000) NT=4 on 256
 # compute units, the full-size workload NT=5
+# K = 64 per LDS stage: odd stage counts at K = 64, 192 and 320
 @pytest.mark.parametrize("m,k,n", [(1, 64, 1), (17, 128, 33), (130, 256, 257), (129, 4096, 321), (300, 1280, 650),
-                                   (512, 64, 1000), (128, 128, 40000), (256, 256, 30000), (3, 8192, 70)])
+                                   (512, 64, 1000), (128, 128, 40000), (256, 256, 30000), (3, 8192, 70),
+                                   (40, 192, 100), (129, 320, 330)])
 def test_f16_gemm_matches_oracle(bqm, m, k, n):
     _, _, w16, x16, y = gemm_case(bqm, m, k, n, seed=m + 3 * k + n)
     y_ref, T = oracle.f16_gemm(w16, x16)

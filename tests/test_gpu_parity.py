@@ -342,8 +342,10 @@ def e4m3_gemm_case(bqm, m, k, n, seed):
     return codes, xq_ref, sc_ref, y.cpu().numpy()
 
 
+# K = 128 per LDS stage: one, two, three (K=384) and five (K=640) stages, the
+# odd counts ending after the loop
 @pytest.mark.parametrize("m,k,n", [(1, 128, 1), (17, 128, 33), (130, 256, 257), (64, 4096, 640),
-                                   (200, 1024, 129)])
+                                   (200, 1024, 129), (33, 384, 97), (129, 640, 330)])
 def test_e4m3_gemm_matches_oracle(bqm, m, k, n):
     codes, xq_ref, sc_ref, y = e4m3_gemm_case(bqm, m, k, n, seed=m + k + n)
     y_ref, T = oracle.e4m3_matmul(codes, xq_ref, sc_ref)
