@@ -81,8 +81,9 @@ def timed_loop(torch, stream, steps, fns):
     The launches are captured once into a HIP graph (torch.cuda.graph) and
     replayed, so host-side launch overhead is out of the measurement: the
     kernels run back to back as they would inside an engine's decode step.
-    The step time comes from events on the replay stream around one replay of
-    the ``steps`` passes.  Each callable's duration comes from a second graph
+    Untimed replays run first until three in a row agree within 0.5% (the
+    clocks have settled); the step time then comes from events on the replay
+    stream around one replay of the ``steps`` passes.  Each callable's duration comes from a second graph
     that launches it ``steps`` times back to back, timed the same way.
     Returns (total ms of the step loop, {name: mean ms per call})."""
     def capture(calls):
@@ -98,18 +99,26 @@ def timed_loop(torch, stream, steps, fns):
         torch.cuda.synchronize()
         return g
 
-    def replay_ms(g, reps=1):
+    def one_replay(g):
         rs = torch.cuda.current_stream()
-        g.replay()                          # warm replay
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(rs)
+        g.replay()
+        b.record(rs)
         torch.cuda.synchronize()
-        times = []
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(rs)
-            g.replay()
-            b.record(rs)
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b))
+        return a.elapsed_time(b)
+
+    def replay_ms(g, reps=1):
+        # untimed warm replays until the clocks have settled: at least 50 ms
+        # of GPU work and three replays in a row within 0.5% of each other
+        # (at most 2 s), so a short --warmup does not time ramping clocks
+        hist, t_end = [one_replay(g)], time.perf_counter() + 2.0
+        while time.perf_counter() < t_end:
+            hist.append(one_replay(g))
+            last = hist[-3:]
+            if len(hist) >= 4 and sum(hist[1:]) >= 50.0 and max(last) <= 1.005 * min(last):
+                break
+        times = [one_replay(g) for _ in range(reps)]
         return sorted(times)[len(times) // 2]
 
     # the step loop: exactly `steps` passes, timed once; each kernel: the
@@ -117,6 +126,130 @@ def timed_loop(torch, stream, steps, fns):
     total_ms = replay_ms(capture([fn for _, fn in fns]))
     per = {name: replay_ms(capture([fn]), reps=9) / steps for name, fn in fns}
     return total_ms, per
+
+
+# the accumulator instrument's two shape sheets (accprobe_bench.rs, fn main:
+# shapes_27b and shapes_1p7b), (in_f, out_f, projection)
+ACCPROBE_LABELS_27B = [(5120, 12288, "q_proj"), (5120, 1024, "k/v_proj"), (6144, 5120, "o_proj"),
+                       (5120, 17408, "gate/up_proj"), (17408, 5120, "down_proj"), (5120, 5120, "square-ref")]
+ACCPROBE_LABELS_1P7B = [(2048, 2048, "q_proj"), (2048, 1024, "k/v_proj"), (2048, 2048, "o_proj"),
+                        (2048, 6144, "gate/up_proj"), (6144, 2048, "down_proj")]
+
+
+def host_description(threads):
+    """The host the CPU oracle ran on: logical CPUs, OpenMP threads, model."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_count": os.cpu_count(), "omp_threads": threads, "model": model,
+            "sched_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def cpu_oracle_legs(single: bool):
+    """Time the CPU oracle (plain C, OpenMP over output rows) on the measured
+    workloads, on whatever OpenMP team this process has.  Each entry gives
+    the rate in the GPU row's own unit.  The m=512 GEMMs run once at full
+    size with the host's threads; on one thread they run on the first 1024
+    weight rows only (the full size would take minutes), which the entry says.
+    Bounded: about 15 s with 16 threads, about 15 s on one."""
+    import oracle
+    import workloads
+
+    res = {"threads": oracle.num_threads()}
+
+    def loop(fn, seconds):
+        r, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            r += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds:
+                return r, dt
+
+    # decode head step (quantize + GEMV, m=1, K=4096, N=64448): the headline's workload
+    m, k, n = 1, 4096, 64448
+    w = workloads.q8_0_weights(n, k, np.random.default_rng(0))
+    x = workloads.activations(m, k, np.random.default_rng(1))
+
+    def head():
+        q, d = oracle.q8_1_quantize(x)
+        oracle.q8_0_matmul(w, q, d, k)
+    r, dt = loop(head, 3.0 if single else 4.0)
+    byts = n * (k // 32) * 34 + m * k * 4 + m * n * 4
+    res["decode_head_step"] = {"value": round(r * byts / dt / 1e9, 2), "unit": "GB/s",
+                               "sample": f"the decode-head step (q8_1 quantize + Q8_0 matmul, m=1, K=4096, "
+                                         f"N=64448) repeated {r} times in {dt:.1f} s"}
+    del w
+
+    # GEMV m=1, 4096 -> 4096 step: median of 3 timed loops
+    m, k, n = 1, 4096, 4096
+    w = workloads.q8_0_weights(n, k, np.random.default_rng(0))
+    x = workloads.activations(m, k, np.random.default_rng(1))
+
+    def gemv():
+        q, d = oracle.q8_1_quantize(x)
+        oracle.q8_0_matmul(w, q, d, k)
+    rates = []
+    for _ in range(3):
+        r, dt = loop(gemv, 0.7)
+        rates.append(r / dt)
+    byts = n * (k // 32) * 34 + m * k * 4 + m * n * 4
+    rate = sorted(rates)[1]
+    res["gemv_m1_4096x4096_step"] = {"value": round(rate * byts / 1e9, 2), "unit": "GB/s",
+                                     "us_per_step": round(1e6 / rate, 1),
+                                     "sample": "q8_1 quantize + Q8_0 matmul, m=1, K=4096, N=4096; median of 3 "
+                                               "loops of >= 0.7 s"}
+
+    # MMQ GEMM m=512, K=4096, N=20480 (1% outliers x10): quantize + matmul, one run
+    m, k, n = 512, 4096, 20480
+    rows = 1024 if single else n
+    w = workloads.q8_0_weights(n, k, np.random.default_rng(0))[:rows]
+    x = workloads.activations(m, k, np.random.default_rng(1), outliers=True)
+    t0 = time.perf_counter()
+    q, d = oracle.q8_1_quantize(x)
+    tq = time.perf_counter() - t0
+    oracle.q8_0_matmul(w, q, d, k)
+    dt = time.perf_counter() - t0
+    ops = 2.0 * m * rows * k
+    res["mmq_m512_n20480"] = {"value": round(ops / dt / 1e9, 2), "unit": "GOPS (2*m*n*k / s)",
+                              "seconds": round(dt, 3), "quantize_s": round(tq, 4),
+                              "sample": f"q8_1 quantize + Q8_0 matmul, m=512, K=4096, "
+                                        f"{'the first 1024 of the' if single else 'all'} 20480 weight rows, one run"}
+    del w
+
+    # FP8 GEMM m=512, K=4096, N=20480: amax quantize + e4m3 matmul, one run
+    codes, w_scale = workloads.e4m3_weights(n, k, np.random.default_rng(0))
+    codes = np.ascontiguousarray(codes[:rows])
+    x = workloads.activations(m, k, np.random.default_rng(1))
+    t0 = time.perf_counter()
+    xq8, sc = oracle.e4m3_quantize_amax(x, w_scale)
+    tq = time.perf_counter() - t0
+    oracle.e4m3_matmul(codes, xq8, sc)
+    dt = time.perf_counter() - t0
+    ops = 2.0 * m * rows * k
+    res["e4m3_m512_n20480"] = {"value": round(ops / dt / 1e9, 2), "unit": "GFLOPS (2*m*n*k / s)",
+                               "seconds": round(dt, 3), "quantize_s": round(tq, 4),
+                               "sample": f"e4m3 amax quantize + fp64 e4m3 matmul, m=512, K=4096, "
+                                         f"{'the first 1024 of the' if single else 'all'} 20480 weight rows, one run"}
+    return res
+
+
+def cpu_single_thread_child():
+    """The CPU legs on one thread, in a child process (OpenMP fixes its team
+    size when a process starts); None if the child fails."""
+    import subprocess
+    try:
+        res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-leg"],
+                             env={**os.environ, "OMP_NUM_THREADS": "1"}, capture_output=True, text=True,
+                             timeout=300)
+        return json.loads(res.stdout.strip().splitlines()[-1])
+    except (subprocess.SubprocessError, ValueError, OSError, IndexError):
+        return None
 
 
 def main():
@@ -130,7 +263,13 @@ def main():
     ap.add_argument("--only", choices=["gemv", "sweep", "mmq", "e4m3", "e4m3_gemv", "f16", "accprobe", "e4m3_blk", "copy"], default=None,
                     help="run one part only (for profiler passes); 'copy' runs a plain 1 GiB device copy "
                          "that calibrates the HBM byte counters")
+    ap.add_argument("--cpu-leg", action="store_true",
+                    help="internal: time the CPU oracle legs on this process's OpenMP team and print JSON "
+                         "(no GPU use)")
     args = ap.parse_args()
+    if args.cpu_leg:
+        print(json.dumps(cpu_oracle_legs(single=True)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
               "(the path shards along N with no exchange; see DESIGN.md)", file=sys.stderr)
@@ -238,6 +377,13 @@ def main():
                 best = min(row.get("one_launch_us", 1e9), row["two_launch_step_us"])
                 gbs = byts / (best * 1e-6) / 1e9
                 row.update({"step_us": best, "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+                # the census convention (decode_kernel_census.rs, fn q8 and fn
+                # report): weight bytes only, per GEMV launch, in TB/s and % of peak
+                wbytes = n * (k // 32) * 34
+                gemv_us = min(row.get("one_launch_us", 1e9), row["two_launch_gemv_us"])
+                row.update({"gemv_us": gemv_us,
+                            "weights_tbs": round(wbytes / (gemv_us * 1e-6) / 1e12, 3),
+                            "weights_pct_peak": round(100 * wbytes / (gemv_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)})
                 sweep[f"m{m} {k}->{n}"] = row
             del ws, w0
         torch.cuda.empty_cache()
@@ -393,83 +539,67 @@ def main():
     if args.only in (None, "accprobe"):
         m, reps, batch = 512, 9, 10
         probe = {}
-        for dist in ("wide", "mid"):
-            cells, ln_sum = {}, 0.0
-            for k, n in workloads.ACCPROBE_SHAPES_27B:
-                log(f"[bench] accprobe {dist} {k}->{n}")
-                w = torch.from_numpy(workloads.accprobe_weights(n, k, rng, dist)).to(dev)
-                xq_h, xds_h = workloads.accprobe_activations(m, k, rng, dist)
-                xq = torch.from_numpy(xq_h).to(dev)
-                xds = torch.from_numpy(xds_h).to(dev)
-                y = torch.empty((m, n), dtype=torch.float32, device=dev)
-                arms = {"f32": lambda: bqm.bqm_q8_0_gemm_f8acc(w, xq, xds, y),
-                        "s32": lambda: bqm.bqm_q8_0_gemm(w, xq, xds, y)}
-                for fn in arms.values():
-                    for _ in range(3):
-                        fn()
-                t = {"f32": [], "s32": []}
-                for _ in range(reps):
-                    for arm in ("f32", "s32"):           # interleaved inside each rep
-                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                        e0.record(stream)
-                        for _ in range(batch):
-                            arms[arm]()
-                        e1.record(stream)
-                        e1.synchronize()
-                        t[arm].append(e0.elapsed_time(e1) / batch)
-                a, b = sorted(t["f32"])[reps // 2], sorted(t["s32"])[reps // 2]
-                ratio = a / b
-                flop = 2.0 * m * k * n
-                cells[f"{k}->{n}"] = {"f32acc_us": round(a * 1e3, 2), "s32acc_us": round(b * 1e3, 2),
-                                      "ratio": round(ratio, 4), "delta_pp": round(100 * (ratio - 1), 1),
-                                      "f32_tflop": round(flop / (a * 1e-3) / 1e12, 1),
-                                      "s32_tflop": round(flop / (b * 1e-3) / 1e12, 1)}
-                ln_sum += np.log(ratio)
-                del w, xq, xds, y
-            geo = float(np.exp(ln_sum / len(cells)))
-            probe[dist] = {"shapes": cells, "geomean_ratio": round(geo, 4), "delta_pp": round(100 * (geo - 1), 1)}
+        sheets = {"27b": ACCPROBE_LABELS_27B, "1p7b": ACCPROBE_LABELS_1P7B}
+        for sheet, shapes in sheets.items():
+            probe[sheet] = {}
+            for dist in ("wide", "mid"):
+                cells, ln_sum = {}, 0.0
+                for k, n, label in shapes:
+                    log(f"[bench] accprobe {sheet} {dist} {label} {k}->{n}")
+                    w = torch.from_numpy(workloads.accprobe_weights(n, k, rng, dist)).to(dev)
+                    xq_h, xds_h = workloads.accprobe_activations(m, k, rng, dist)
+                    xq = torch.from_numpy(xq_h).to(dev)
+                    xds = torch.from_numpy(xds_h).to(dev)
+                    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+                    arms = {"f32": lambda: bqm.bqm_q8_0_gemm_f8acc(w, xq, xds, y),
+                            "s32": lambda: bqm.bqm_q8_0_gemm(w, xq, xds, y)}
+                    for fn in arms.values():
+                        for _ in range(3):
+                            fn()
+                    t = {"f32": [], "s32": []}
+                    for _ in range(reps):
+                        for arm in ("f32", "s32"):           # interleaved inside each rep
+                            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                            e0.record(stream)
+                            for _ in range(batch):
+                                arms[arm]()
+                            e1.record(stream)
+                            e1.synchronize()
+                            t[arm].append(e0.elapsed_time(e1) / batch)
+                    a, b = sorted(t["f32"])[reps // 2], sorted(t["s32"])[reps // 2]
+                    ratio = a / b
+                    flop = 2.0 * m * k * n
+                    cells[f"{label} {k}->{n}"] = {"f32acc_us": round(a * 1e3, 2), "s32acc_us": round(b * 1e3, 2),
+                                                  "ratio": round(ratio, 4), "delta_pp": round(100 * (ratio - 1), 1),
+                                                  "f32_tflop": round(flop / (a * 1e-3) / 1e12, 1),
+                                                  "s32_tflop": round(flop / (b * 1e-3) / 1e12, 1)}
+                    ln_sum += np.log(ratio)
+                    del w, xq, xds, y
+                geo = float(np.exp(ln_sum / len(cells)))
+                probe[sheet][dist] = {"shapes": cells, "geomean_ratio": round(geo, 4),
+                                      "delta_pp": round(100 * (geo - 1), 1)}
         torch.cuda.empty_cache()
-        out["accprobe_m512"] = {"workload": "accumulator instrument, m=512, 27B projection shapes: the MMQ with "
-                                            "int8 MFMA + s32 block sums (s32) vs fp8 MFMA + f32 block sums (f32), "
-                                            "same tiles and fold count; medians of 9 interleaved reps of 10 launches",
+        out["accprobe_m512"] = {"workload": "accumulator instrument, m=512, the 27B and 1.7B projection sheets: the "
+                                            "MMQ with int8 MFMA + s32 block sums (s32) vs fp8 MFMA + f32 block sums "
+                                            "(f32), same tiles and fold count; medians of 9 interleaved reps of 10 "
+                                            "launches, geomean of the ratio per sheet and byte distribution",
                                 **probe}
 
     # ---------------------------------------------------------------- CPU oracle baseline
-    if not args.no_cpu and args.only in (None, "gemv"):
-        import oracle
-
-        m, k, n = 1, 4096, 64448
-        w_host = workloads.q8_0_weights(n, k, np.random.default_rng(0))
-        x_host = workloads.activations(m, k, np.random.default_rng(1))
-        reps, t_total = 0, 0.0
-        t0 = time.perf_counter()
-        while t_total < 10.0 and reps < 5000:
-            xq_h, xds_h = oracle.q8_1_quantize(x_host)
-            oracle.q8_0_matmul(w_host, xq_h, xds_h, k)
-            reps += 1
-            t_total = time.perf_counter() - t0
-        gbs = reps * (q8_0_bytes(m, k, n) + m * k * 4) / t_total / 1e9
-        out["cpu_baseline"] = {"value": round(gbs, 2), "unit": "GB/s", "cores": oracle.num_threads(),
-                               "kind": "oracle",
-                               "sample": f"the full decode-head step (q8_1 quantize + Q8_0 matmul, m=1, "
-                                         f"K=4096, N=64448) repeated {reps} times in {t_total:.1f} s"}
-        # the same on one thread, in a child process (OpenMP fixes its team at start)
-        import subprocess
-        code = ("import sys, time, numpy as np; sys.path.insert(0, %r); import oracle, workloads\n"
-                "w = workloads.q8_0_weights(64448, 4096, np.random.default_rng(0))\n"
-                "x = workloads.activations(1, 4096, np.random.default_rng(1))\n"
-                "r, t0 = 0, time.perf_counter()\n"
-                "while time.perf_counter() - t0 < 5.0:\n"
-                "    q, d = oracle.q8_1_quantize(x); oracle.q8_0_matmul(w, q, d, 4096); r += 1\n"
-                "print(r, time.perf_counter() - t0)\n") % ROOT
-        try:
-            res = subprocess.run([sys.executable, "-c", code], env={**os.environ, "OMP_NUM_THREADS": "1"},
-                                 capture_output=True, text=True, timeout=120)
-            r1, t1 = res.stdout.split()
-            out["cpu_baseline"]["single_thread_value"] = round(
-                int(r1) * (q8_0_bytes(m, k, n) + m * k * 4) / float(t1) / 1e9, 2)
-        except (subprocess.SubprocessError, ValueError, OSError):
-            out["cpu_baseline"]["single_thread_value"] = None
+    if not args.no_cpu and args.only is None:
+        log("[bench] cpu oracle baseline (host threads)")
+        multi = cpu_oracle_legs(single=False)
+        log("[bench] cpu oracle baseline (one thread, child process)")
+        single = cpu_single_thread_child()
+        head = multi["decode_head_step"]
+        out["cpu_baseline"] = {
+            "value": head["value"], "unit": "GB/s", "cores": multi["threads"], "kind": "oracle",
+            "sample": head["sample"],
+            "single_thread_value": (single or {}).get("decode_head_step", {}).get("value"),
+            "host": host_description(multi["threads"]),
+            "configs": {k2: v for k2, v in multi.items() if k2 != "threads"},
+            "single_thread": {k2: v for k2, v in (single or {}).items() if k2 != "threads"} or None,
+        }
 
     print(json.dumps(out), flush=True)
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "bqmm.h"
 
 namespace bqm {
@@ -20,21 +22,71 @@ constexpr int kQ80Bytes = 34;    // Q8_0 block: fp16 scale + 32 int8
 
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Map the last launch status to the library's return code.
+// Map the launch status to the library's return code.  The status is read
+// with hipPeekAtLastError, which leaves it in place: an error the caller left
+// pending before the call is reported (it is indistinguishable from a failed
+// launch) but not consumed.
 inline int launch_status() {
-    hipError_t e = hipGetLastError();
+    hipError_t e = hipPeekAtLastError();
     return e == hipSuccess ? BQM_OK : BQM_EHIP_BASE + (int)e;
 }
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Host-side facts that the launches need are queried once per device and
+// kept in per-device slots (a device ordinal beyond the table shares the last
+// slot and is re-queried whenever its value differs).
+constexpr int kMaxDevices = 64;
+
+inline int current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    return dev < kMaxDevices ? dev : kMaxDevices - 1;
+}
+
 // Compute units of the current device (256 on MI355X, also the fallback).
 inline int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        cus = 256;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    const int slot = dev < kMaxDevices ? dev : kMaxDevices - 1;
+    int cus = dev < kMaxDevices ? cache[slot].load(std::memory_order_relaxed) : 0;
+    if (cus > 0) return cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    if (dev < kMaxDevices) cache[slot].store(cus, std::memory_order_relaxed);
     return cus;
+}
+
+// Per-kernel launch facts: whether the dynamic LDS limit has been raised on a
+// device, and the last occupancy answer (for one LDS size) on each device.
+// One static instance per kernel instantiation.
+struct LaunchCache {
+    std::atomic<int> lds_raised[kMaxDevices];
+    std::atomic<uint64_t> occupancy[kMaxDevices];   // (lds bytes << 8) | blocks per CU, 0 = none
+};
+
+// Allow `bytes` of dynamic LDS for kernel `fn` on the current device (once).
+inline int raise_lds_limit(LaunchCache &c, const void *fn, int bytes) {
+    const int dev = current_device();
+    if (c.lds_raised[dev].load(std::memory_order_relaxed)) return BQM_OK;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
+    c.lds_raised[dev].store(1, std::memory_order_relaxed);
+    return BQM_OK;
+}
+
+// Resident workgroups per CU of `fn` with `threads` threads and `lds` bytes of
+// dynamic LDS, at least 1 and at most `cap`; asked of the runtime only when the
+// LDS size differs from the last one asked on this device.
+inline int blocks_per_cu(LaunchCache &c, const void *fn, int threads, int lds, int cap) {
+    const int dev = current_device();
+    const uint64_t hit = c.occupancy[dev].load(std::memory_order_relaxed);
+    if (hit != 0 && (hit >> 8) == (uint64_t)(uint32_t)lds) return (int)(hit & 0xFF);
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess || per_cu < 1) per_cu = 1;
+    if (per_cu > cap) per_cu = cap;
+    c.occupancy[dev].store(((uint64_t)(uint32_t)lds << 8) | (uint64_t)per_cu, std::memory_order_relaxed);
+    return per_cu;
 }
 
 // The matrix-core GEMV for 3..15 tokens (q8_0_gemv_mma.hip): whether it takes

@@ -2,11 +2,12 @@
 // e4m3 x e4m3 GEMM with f32 accumulation.
 //
 // From the "fp8_ffi.rs" page (memra-engine 0.70.0), module doc, fn
-// try_fp8_gemm and the Fp8Scratch doc: the activation is quantized f32 ->
-// e4m3 with ONE per-batch scale amax/448 reduced on the device; the act scale
-// and the per-tensor weight_scale are folded into one device scalar that the
-// GEMM reads by pointer (scale block [0]=amax, [1]=quant mul, [2]=folded);
-// y[m,out] = x[m,in] @ (e4m3 W)^T, no host synchronization anywhere.
+// try_fp8_gemm and the Fp8Scratch doc: the whole activation batch shares a
+// single e4m3 scale, amax/448, whose amax is reduced on the device; that
+// scale times the per-tensor weight_scale is one device scalar the GEMM reads
+// through a pointer (the scale block keeps the amax, the quantization
+// multiplier and this folded scale, in that order); the output is the
+// activation times the transposed e4m3 weight, with no host synchronization.
 //
 // Quantization is three launches on the caller's stream, with no atomics and
 // no scratch allocation:

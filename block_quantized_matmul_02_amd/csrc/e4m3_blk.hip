@@ -1,6 +1,6 @@
 // Block-128 FP8 prefill path for gfx950: the e4m3 NaN-code count of a weight,
 // the per-(token, 128-k block) activation quantization, and the per-block FP8
-// GEMM that folds once per 128-k block.
+// GEMM that applies the block scales a single time per 128 values of k.
 //
 // From the "fp8_ffi.rs" page (memra-engine 0.70.0), the per-block FP8 MMQ
 // section (try_fp8_blk_mmq, fp8_mmq_enabled and FP8_MMQ_NAN_OK docs): the

@@ -464,20 +464,13 @@ template <int JM, bool XREG, int NT>
 static int e8_launch(const uint8_t *w, const float *x, float w_scale, float *y, int m, int k, int n,
                      const E8Geom &g, hipStream_t stream) {
     const int lds = XREG ? 0 : g.tgsz * k * 4;
-    static int attr_done = 0;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&e4m3_gemv_kernel<JM, XREG, NT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kE8LdsBytes);
-        if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
-        attr_done = 1;
-    }
+    static LaunchCache cache;
+    const void *fn = reinterpret_cast<const void *>(&e4m3_gemv_kernel<JM, XREG, NT>);
+    const int rc = raise_lds_limit(cache, fn, kE8LdsBytes);
+    if (rc != BQM_OK) return rc;
     const int cus = device_cus();
     // resident workgroups per CU (registers and LDS), at most 4
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&e4m3_gemv_kernel<JM, XREG, NT>),
-                                                     NT, lds) != hipSuccess || per_cu < 1)
-        per_cu = 1;
-    if (per_cu > 4) per_cu = 4;
+    const int per_cu = blocks_per_cu(cache, fn, NT, lds, 4);
     // Workgroups per token group: no more than fit at once, and few enough
     // that each wave has at least four items (two in the large workgroups,
     // whose staged tokens are shared by 8 or 16 waves).
@@ -504,18 +497,11 @@ static int e8_launch_slots(const uint8_t *w, const float *x, float w_scale, floa
                            const E8Geom &g, hipStream_t stream) {
     constexpr int NT = 64 * JP;
     const int lds = 2 * JP * MT * JP * 64 * 4;
-    static int attr_done = 0;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&e4m3_gemv_slots_kernel<JP, MT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kE8LdsBytes);
-        if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
-        attr_done = 1;
-    }
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&e4m3_gemv_slots_kernel<JP, MT>),
-                                                     NT, lds) != hipSuccess || per_cu < 1)
-        per_cu = 1;
-    if (per_cu > 4) per_cu = 4;
+    static LaunchCache cache;
+    const void *fn = reinterpret_cast<const void *>(&e4m3_gemv_slots_kernel<JP, MT>);
+    const int rc = raise_lds_limit(cache, fn, kE8LdsBytes);
+    if (rc != BQM_OK) return rc;
+    const int per_cu = blocks_per_cu(cache, fn, NT, lds, 4);
     // row workgroups per token group: all that fit at once, but at least 4
     // items each (every workgroup also loads the group's activations once)
     const int n_items = (n + JP - 1) / JP;

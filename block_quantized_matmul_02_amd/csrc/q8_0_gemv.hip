@@ -12,7 +12,7 @@
 //    Each row is handled by L lanes (L = next power of two >= P, at most
 //    64); lane i of the row owns pairs i, i+L, ...  A wave covers G = 64/L
 //    rows per row-step.
-//  * A wave streams a tile of RT whole rows (<= 12 KiB) with 16-byte buffer
+//  * A wave streams a tile of RT whole rows (<= 5 KiB) with 16-byte buffer
 //    loads: slot s of lane l loads chunk 64*s + l of the tile, so every load
 //    instruction reads 1 KiB of consecutive bytes.  Buffer loads check the
 //    range in hardware: rows past n and unused slots read zeros, never fault.
@@ -477,13 +477,10 @@ static bool make_geom(int k, int n, int64_t w_row_bytes, GemvGeom &g) {
 template <int M, bool SINGLE, int PRE, bool QX, bool XR>
 static int launch_variant(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
                           float *y, int k, int n, const GemvGeom &g, int grid, int lds_bytes, hipStream_t stream) {
-    static int attr_done = 0;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, SINGLE, PRE, QX, XR>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
-        attr_done = 1;
-    }
+    static LaunchCache cache;
+    const int rc = raise_lds_limit(cache, reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, SINGLE, PRE, QX, XR>),
+                                   160 * 1024);
+    if (rc != BQM_OK) return rc;
     hipLaunchKernelGGL((q8_0_gemv_kernel<M, SINGLE, PRE, QX, XR>), dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w,
                        w_row_bytes, xq, xds, x, y, k, n, g);
     return launch_status();
@@ -493,19 +490,10 @@ static int launch_variant(const uint8_t *w, int64_t w_row_bytes, const int8_t *x
 // at most 4.
 template <int M, int PRE, bool QX, bool XR>
 static int gemv_per_cu(int lds_bytes) {
-    static int attr_done = 0;   // allow up to 160 KiB of LDS before asking
-    if (!attr_done) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE, QX, XR>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-            return 1;
-        attr_done = 1;
-    }
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu,
-                                                     reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE, QX, XR>),
-                                                     kGemvThreads, lds_bytes) != hipSuccess || per_cu < 1)
-        per_cu = 1;
-    return per_cu > 4 ? 4 : per_cu;
+    static LaunchCache cache;
+    const void *fn = reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE, QX, XR>);
+    if (raise_lds_limit(cache, fn, 160 * 1024) != BQM_OK) return 1;   // allow up to 160 KiB before asking
+    return blocks_per_cu(cache, fn, kGemvThreads, lds_bytes, 4);
 }
 
 // Grid size and the pipelined / single-item choice, then the launch.

@@ -323,13 +323,9 @@ template <int M>
 static int launch_mma(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y, int k, int n,
                       const MvGeom &g, hipStream_t stream) {
     const int lds_bytes = g.act_bytes + kMvWaves * kMvTileBytes + kMvCombBytes;
-    static int attr_done = 0;
-    if (!attr_done) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q8_0_gemv_mma_kernel<M>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return BQM_EHIP_BASE + (int)e;
-        attr_done = 1;
-    }
+    static LaunchCache cache;
+    const int rc = raise_lds_limit(cache, reinterpret_cast<const void *>(&q8_0_gemv_mma_kernel<M>), 160 * 1024);
+    if (rc != BQM_OK) return rc;
     // persistent workgroups, one per CU, as few as give each the same number of iterations
     int grid = device_cus();
     if (g.iters < grid) grid = g.iters;

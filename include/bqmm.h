@@ -23,9 +23,12 @@
  *     range; BQM_EUNSUPPORTED for a shape or alignment the kernels do not
  *     handle; BQM_EHIP_BASE + hipError_t when a launch fails.  Argument
  *     checks run before any HIP call, so a rejected call touches neither
- *     the device nor the stream.  A launch error is read with
- *     hipGetLastError(), so an error left pending by the caller's own
- *     earlier HIP calls is reported here too.
+ *     the device nor the stream.  After its launches a call reads the
+ *     runtime's error state with hipPeekAtLastError(), which leaves the
+ *     state in place: a failed launch stays pending for the caller to
+ *     clear with hipGetLastError(), and an error the caller left pending
+ *     before the call is reported by the call as well (the two cannot be
+ *     told apart without consuming the caller's error).
  *   - Calls on one stream run in order; calls on different streams that
  *     write the same buffer race (the library has no internal state).
  *
@@ -54,10 +57,11 @@ extern "C" {
 
 /*
  * q8_1 activation quantization, per token and 32-value block
- * ("decode_kernel_census.rs", fn q8: one int8 per column plus a pair of f32
- * per 32-block; the int8 rule d = amax/127, q = clamp(round(x/d), -127, 127)
- * with round half away from zero follows "f16_ffi.rs", fn try_f16_gemm,
- * W8A8 arm; "accprobe_bench.rs" module doc: +-127 at every block amax).
+ * ("decode_kernel_census.rs", fn q8: an int8 for every value and two f32
+ * numbers for every 32-value block; the int8 rule d = amax/127, q =
+ * clamp(round(x/d), -127, 127) with round half away from zero follows
+ * "f16_ffi.rs", fn try_f16_gemm, W8A8 arm; "accprobe_bench.rs" module doc:
+ * a block's largest magnitude always maps to +-127).
  *
  *   x   : f32 [m][k], 16-byte aligned.
  *   xq  : int8 [m][k] out, 4-byte aligned.
@@ -133,10 +137,11 @@ int bqm_q8_0_gemm_f8acc(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq,
                         float *y, int m, int k, int n, void *stream);
 
 /*
- * Per-batch e4m3 activation quantization ("fp8_ffi.rs" module doc: f32 ->
- * e4m3 with one per-batch scalar scale amax/448, device amax reduce, the
- * scale folded with weight_scale into a device scalar, no host sync;
- * Fp8Scratch doc: scale block [0]=amax, [1]=quant mul, [2]=folded scale).
+ * Per-batch e4m3 activation quantization ("fp8_ffi.rs" module doc: the
+ * batch shares one e4m3 scale, amax/448, with the amax reduced on the device
+ * and the scale multiplied by weight_scale into a device scalar, with no host
+ * synchronization; Fp8Scratch doc: the scale block keeps the amax, the
+ * quantization multiplier and the folded scale, in that order).
  *
  *   x       : f32 [m][k], 16-byte aligned.
  *   xq      : uint8 [m][k] OCP E4M3FN codes out, 4-byte aligned.
@@ -153,9 +158,10 @@ int bqm_e4m3_quantize_amax(const float *x, uint8_t *xq, float *scales, float w_s
                            int k, void *stream);
 
 /*
- * FP8-E4M3 prefill GEMM ("fp8_ffi.rs" module doc and fn try_fp8_gemm:
- * y[m,out] = x[m,in] @ (e4m3 W)^T, the act scale and weight_scale folded
- * into one device scalar read by pointer, f32 accumulate).
+ * FP8-E4M3 prefill GEMM ("fp8_ffi.rs" module doc and fn try_fp8_gemm: the
+ * activation times the transposed e4m3 weight, with the activation scale and
+ * weight_scale combined into one device scalar read through a pointer, and
+ * f32 accumulation).
  *
  *   w      : uint8 E4M3FN codes [n][k], 16-byte aligned.
  *   xq     : uint8 E4M3FN codes [m][k], 16-byte aligned.
@@ -229,7 +235,8 @@ int bqm_f16_gemm(const uint16_t *w16, const uint16_t *x16, float *y, int m, int 
  * per-block FP8 MMQ section: try_fp8_blk_mmq, fp8_mmq_enabled and
  * FP8_MMQ_NAN_OK docs).  The weight is the checkpoint's e4m3 codes with a
  * row-major f32 grid of one scale per 128x128 block and no per-tensor scale;
- * the kernel folds once per 128-k block ("accprobe_bench.rs" module doc).
+ * the kernel applies the scales once per 128 values of k ("accprobe_bench.rs"
+ * module doc).
  *
  * bqm_e4m3_nan_count: *nan_count = number of bytes of w[0..count) whose low
  * 7 bits are all ones (the e4m3 NaN codes 0x7F / 0xFF, which the matrix cores

@@ -15,20 +15,22 @@
  *  - Q8_0 weight block = fp16 scale + 32 int8 quants, 34 bytes; a row is
  *    in_f/32 blocks: "decode_kernel_census.rs" (0.113.0), fn q8;
  *    "accprobe_bench.rs" (0.124.1), fn synth_w_q8_0.
- *  - q8_1 activation = one int8 per column + a pair of f32 per 32-block:
- *    "decode_kernel_census.rs", fn q8.
+ *  - q8_1 activation: an int8 quant for every value and two f32 numbers
+ *    for every 32-value block: "decode_kernel_census.rs", fn q8.
  *  - int8 quantization d = amax/127, q = clamp(round(v/d), -127, 127) with
  *    Rust's round (half away from zero): "f16_ffi.rs" (0.81.0), fn
- *    try_f16_gemm (the W8A8 simulation arm); "an int8 quantizer emits +-127
- *    at every block amax": "accprobe_bench.rs", module doc.
+ *    try_f16_gemm (the W8A8 simulation arm); the value with the largest
+ *    magnitude in a block always becomes +127 or -127: "accprobe_bench.rs",
+ *    module doc.
  *  - s32 accumulate per 32-block, folded into f32 by the two scales:
  *    "accprobe_bench.rs", module doc (the floor folds every k32).
  *  - e4m3: 0x7F magnitude is NaN ("accprobe_bench.rs" module doc;
  *    "fp8_ffi.rs" (0.70.0), FP8_MMQ_NAN_OK doc), codes 0x01-0x07 are
  *    denormals ("accprobe_bench.rs", fn synth_w_q8_0 doc); activation scale
  *    amax/448 per batch, one scalar, folded with weight_scale into a device
- *    scalar read by the GEMM; scale block [0]=amax, [1]=quant mul,
- *    [2]=folded scale ("fp8_ffi.rs", module doc and Fp8Scratch doc).
+ *    scalar read by the GEMM; the device scale block holds the amax, then the
+ *    quantization multiplier, then the folded scale ("fp8_ffi.rs", module
+ *    doc and Fp8Scratch doc).
  *
  * Readings where the pages are silent are listed beside each function.
  */
@@ -476,8 +478,8 @@ void oracle_q8_0_matmul_e4m3(const uint8_t *w, int64_t row_bytes, const uint8_t 
  * Block-128 FP8 operands ("fp8_ffi.rs" page, memra-engine 0.70.0, the
  * per-block FP8 MMQ section: try_fp8_blk_mmq, fp8_mmq_enabled and the
  * FP8_MMQ_NAN_OK docs; "accprobe_bench.rs" module doc: the per-block kernel
- * chains its k32 products into one accumulator and folds once per 128-k
- * block).  The weight is e4m3 codes [n][k] with a row-major f32 grid
+ * sums the four k32 steps of a 128-k block in one accumulator and applies
+ * the block's scales a single time).  The weight is e4m3 codes [n][k] with a row-major f32 grid
  * [ceil(n/128)][ceil(k/128)], one scale per 128x128 block, and a per-tensor
  * scale of 1.  Magnitude 0x7F is NaN to the hardware, so a weight holding
  * one is refused after a one-time count.

@@ -35,7 +35,8 @@ per-block MMQ section: e4m3 codes plus a row-major f32 grid
 ``accprobe_weights`` / ``accprobe_activations`` (the accumulator
 instrument's quantizer-free bytes, "accprobe_bench.rs" page (memra-engine
 0.124.1), fns ``synth_w_q8_0`` and ``synth_act_q8_1``: quant magnitudes at
-most 126, so every byte is finite and non-NaN read as int8 or as e4m3):
+most 126, so no byte is a NaN or non-finite value whether read as int8 or as
+e4m3):
 quants first -- ``wide``: ``integers(-126, 126, (N, K))`` with every value
 ``v >= -1`` moved up by one, i.e. uniform over -126..126 without -1 (int8 -1
 is byte 0xFF, which the page's own magnitude clamp lets through although it is
