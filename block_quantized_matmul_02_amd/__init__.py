@@ -49,6 +49,7 @@ def lib() -> ctypes.CDLL:
         L.bqm_e4m3_blk_gemm.argtypes = [P, P, P, P, P, I, I, I, P]
         L.bqm_e4m3_quantize_amax.argtypes = [P, P, P, F, I, I, P]
         L.bqm_e4m3_gemm.argtypes = [P, P, P, P, I, I, I, P]
+        L.bqm_e4m3_gemm_exact.argtypes = [P, P, P, P, I, I, I, P]
         L.bqm_e4m3_gemv.argtypes = [P, P, F, P, I, I, I, P]
         L.bqm_q8_0_dequant_f16.argtypes = [P, I64, P, I, I, P]
         L.bqm_f16_cvt.argtypes = [P, P, I64, P]
@@ -56,7 +57,7 @@ def lib() -> ctypes.CDLL:
         for fn in ("bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax",
                    "bqm_e4m3_gemm", "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm",
                    "bqm_q8_0_gemm_f8acc", "bqm_e4m3_nan_count", "bqm_e4m3_blk_quantize", "bqm_e4m3_blk_gemm",
-                   "bqm_q8_0_gemv_f32"):
+                   "bqm_q8_0_gemv_f32", "bqm_e4m3_gemm_exact"):
             getattr(L, fn).restype = ctypes.c_int
         L.bqm_strerror.argtypes = [I]
         L.bqm_strerror.restype = ctypes.c_char_p
@@ -203,6 +204,24 @@ def bqm_e4m3_gemm(w, xq, scales, y=None):
     _check(y, torch.float32, "y", (m, n))
     rc = lib().bqm_e4m3_gemm(_ptr(w), _ptr(xq), _ptr(scales), _ptr(y), m, k, n, _stream(w))
     _raise("bqm_e4m3_gemm", rc)
+    return y
+
+
+def bqm_e4m3_gemm_exact(w, xq, scales, y=None):
+    """e4m3 GEMM with the bound (27 + k/128) * 2^-24 * sum|terms| on every output: same arguments and
+    result as :func:`bqm_e4m3_gemm`."""
+    import torch
+
+    n, k = w.shape
+    m = xq.shape[0]
+    _check(w, torch.uint8, "w")
+    _check(xq, torch.uint8, "xq", (m, k))
+    _check(scales, torch.float32, "scales", (4,))
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _check(y, torch.float32, "y", (m, n))
+    rc = lib().bqm_e4m3_gemm_exact(_ptr(w), _ptr(xq), _ptr(scales), _ptr(y), m, k, n, _stream(w))
+    _raise("bqm_e4m3_gemm_exact", rc)
     return y
 
 

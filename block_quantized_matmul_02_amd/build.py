@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libbqmm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["q8_1_quantize.hip", "q8_0_gemv.hip", "q8_0_gemv_mma.hip", "q8_0_gemm.hip", "e4m3.hip", "e4m3_gemv.hip", "f16_mirror.hip", "e4m3_blk.hip", "strerror.cpp"]
+SOURCES = ["q8_1_quantize.hip", "q8_0_gemv.hip", "q8_0_gemv_mma.hip", "q8_0_gemm.hip", "e4m3.hip", "e4m3_exact.hip", "e4m3_gemv.hip", "f16_mirror.hip", "e4m3_blk.hip", "strerror.cpp"]
 
 HIPFLAGS = [
     f"--offload-arch={ARCH}",
@@ -43,6 +43,7 @@ HIPFLAGS = [
 EXTRA = {
     "q8_0_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "q8_0_gemv_mma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "e4m3_exact.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

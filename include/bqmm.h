@@ -175,6 +175,24 @@ int bqm_e4m3_gemm(const uint8_t *w, const uint8_t *xq, const float *scales, floa
                   int k, int n, void *stream);
 
 /*
+ * The FP8-E4M3 prefill GEMM of bqm_e4m3_gemm ("fp8_ffi.rs" module doc and fn
+ * try_fp8_gemm: the same result, y[t][r] = scales[2] * sum_k dec(xq[t][k]) *
+ * dec(w[r][k]), f32 accumulation), computed with an error bound that holds
+ * for any data: every output is within (27 + k/128) * 2^-24 * T of the exact
+ * value, T = |scales[2]| * sum_k |dec(xq[t][k]) * dec(w[r][k])|, i.e. within
+ * 1e-5 * T for every accepted k.  bqm_e4m3_gemm runs on the fp8 matrix
+ * cores, whose summation cuts products 13 bits below the largest of each
+ * 8-byte group (worst case about 8.5e-4 * T); this call converts the codes
+ * exactly to fp16 and runs the fp16 matrix cores (24 bits kept per group),
+ * summing each 128-k stage into a fresh partial, at roughly half the speed.
+ *
+ *   Arguments, layouts, alignment and NaN-code rule as bqm_e4m3_gemm.
+ *   k % 128 == 0 and k <= 16384 (else BQM_EUNSUPPORTED).
+ */
+int bqm_e4m3_gemm_exact(const uint8_t *w, const uint8_t *xq, const float *scales, float *y, int m,
+                        int k, int n, void *stream);
+
+/*
  * e4m3 decode GEMV on raw e4m3 weights with a per-tensor scale ("fp8_ffi.rs"
  * st_e4m3_enabled doc: decode reads the checkpoint's own e4m3 bytes through
  * qmatvec_e4m3_mmvq, for the per-tensor scalar-scale class).  The pages do

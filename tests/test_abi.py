@@ -33,7 +33,8 @@ def test_header_declares_the_calls_and_strerror():
     assert declared_symbols() == sorted([
         "bqm_q8_1_quantize", "bqm_q8_0_gemv", "bqm_q8_0_gemm", "bqm_e4m3_quantize_amax", "bqm_e4m3_gemm",
         "bqm_e4m3_gemv", "bqm_q8_0_dequant_f16", "bqm_f16_cvt", "bqm_f16_gemm", "bqm_q8_0_gemm_f8acc",
-        "bqm_e4m3_nan_count", "bqm_e4m3_blk_quantize", "bqm_e4m3_blk_gemm", "bqm_q8_0_gemv_f32", "bqm_strerror"])
+        "bqm_e4m3_nan_count", "bqm_e4m3_blk_quantize", "bqm_e4m3_blk_gemm", "bqm_q8_0_gemv_f32",
+        "bqm_e4m3_gemm_exact", "bqm_strerror"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -133,6 +134,16 @@ def test_e4m3_validation(L):
     assert g(A16, B16, C16, D16, 1, 128, 0, NUL) == 1
     assert g(A16, B16, C16, D16, 1, 192, 8, NUL) == 2                  # k % 128
     assert g(A16, MIS2, C16, D16, 1, 128, 8, NUL) == 2
+    x = L.bqm_e4m3_gemm_exact
+    assert x(NUL, B16, C16, D16, 1, 128, 8, NUL) == 1
+    assert x(A16, B16, NUL, D16, 1, 128, 8, NUL) == 1
+    assert x(A16, B16, C16, D16, 0, 128, 8, NUL) == 1
+    assert x(A16, B16, C16, D16, 1, 64, 8, NUL) == 1                   # k < 128
+    assert x(A16, B16, C16, D16, 1, 128, 0, NUL) == 1
+    assert x(A16, B16, C16, D16, 1, 192, 8, NUL) == 2                  # k % 128
+    assert x(A16, B16, C16, D16, 1, 16384 + 128, 8, NUL) == 2          # k beyond the bound's range
+    assert x(A16, MIS2, C16, D16, 1, 128, 8, NUL) == 2
+    assert x(A16, B16, C16, MIS2, 1, 128, 8, NUL) == 2                 # y 4-byte alignment
 
 
 def test_e4m3_gemv_validation(L):

@@ -3,7 +3,9 @@
 Bar: int8 quants, e4m3 codes and every scale are bit-exact; int32 block sums
 are exact (checked through unit-scale and one-hot cases where y is an exact
 integer); f32 outputs are within 1e-5 * sum|terms| per element, and exactly 0
-where sum|terms| is 0.  Outputs are pre-filled with NaN to prove they are
+where sum|terms| is 0 -- except the fp8-core e4m3 GEMM, whose bound derived
+from the matrix cores' summation is given below (its bounded twin on the fp16
+cores meets 1e-5 by construction).  Outputs are pre-filled with NaN to prove they are
 fully overwritten.  The full-size GEMV and m=512 GEMM workloads are checked
 on every output.
 """
@@ -39,18 +41,33 @@ def nan_like_out(m, n):
     return torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
 
 
-# The fp8 matrix cores do not accumulate at f32 precision: measured on gfx950,
-# one 64-deep v_mfma_scale_f32_32x32x64_f8f6f4 step errs by up to 3.4e-5 of the
-# sum of |products| it adds (median 1.1e-6; products are summed in groups of 16
-# with truncation relative to the group's largest product).  The bound of the
-# method, 1e-5 * sum|terms|, holds once K spans many such steps (the FP8
-# workload has K = 4096: 64 steps whose errors average out); for K <= 512 the
-# tests use the measured single-step bound instead.
-FP8_STEP_BOUND = 4e-5
+# Error bounds of the two FP8-E4M3 GEMMs, derived from the matrix cores'
+# summation as measured on gfx950 (u = 2^-24, T = sum of |terms| of an output,
+# the folded scale included):
+#  * bqm_e4m3_gemm, on v_mfma_scale_f32_32x32x64_f8f6f4: the eight products of
+#    each 8-byte group a lane supplies are aligned to the largest and cut 13
+#    bits below its leading bit, toward zero (pinned below through the C ABI),
+#    so a group errs by less than 7 * 2^-13 of its largest product; group sums
+#    and the accumulator are added in f32 (at most 8 roundings per 64-deep
+#    step), and the epilogue multiplies once:
+#        (7 * 2^-13 + (8 * k/64 + 1) * u) * T     -- 8.8e-4 * T at k = 4096.
+#    This is above the method's 1e-5 * T: the fp8 path meets 1e-5 only where
+#    the data keep each group's truncated products small (the seeded FP8
+#    workload does; the observed maxima are printed).
+#  * bqm_e4m3_gemm_exact, on v_mfma_f32_32x32x16_f16 with the codes converted
+#    exactly to fp16 (24 bits kept per group, group sums rounded to nearest)
+#    and a fresh f32 partial per 128-k stage:
+#        (27 + k/128) * u * T                      -- 3.5e-6 * T at k = 4096,
+#    below 1e-5 * T for every k it accepts (<= 16384).
+def fp8_bound(k):
+    return 7 * 2.0 ** -13 + (8 * (k // 64) + 1) * 2.0 ** -24
 
 
-def e4m3_tolerance(k):
-    return 1e-5 if k >= 1024 else FP8_STEP_BOUND
+def exact_bound(k):
+    return (27 + k / 128) * 2.0 ** -24
+
+
+E4M3_GEMMS = {"fp8": ("bqm_e4m3_gemm", fp8_bound), "exact": ("bqm_e4m3_gemm_exact", exact_bound)}
 
 
 def assert_fold_close(y_gpu, y_ref, T, what, tol=1e-5):
@@ -60,7 +77,9 @@ def assert_fold_close(y_gpu, y_ref, T, what, tol=1e-5):
     zero = T == 0
     assert np.all(y[zero] == 0), f"{what}: nonzero output where all terms are 0"
     ratio = err[~zero] / T[~zero]
-    assert ratio.size == 0 or ratio.max() <= tol, f"{what}: max err/sum|terms| = {ratio.max():.3e} > {tol}"
+    worst = float(ratio.max()) if ratio.size else 0.0
+    assert worst <= tol, f"{what}: max err/sum|terms| = {worst:.3e} > {tol}"
+    return worst
 
 
 def quantize_both(bqm, x):
@@ -322,28 +341,40 @@ def test_e4m3_quantize_constant_and_zero_batches(bqm):
     assert np.array_equal(xq.cpu().numpy(), xq_ref) and np.all(sc.cpu().numpy() == 0)
 
 
-def e4m3_gemm_case(bqm, m, k, n, seed):
+def e4m3_gemm_case(bqm, m, k, n, seed, kernel="fp8", act=None):
     rng = np.random.default_rng(seed)
     codes, w_scale = workloads.e4m3_weights(n, k, rng)
-    x = workloads.activations(m, k, rng)
+    x = workloads.activations(m, k, rng) if act is None else act(m, k, rng)
     xq, sc, xq_ref, sc_ref = e4m3_quantize_both(bqm, x, w_scale)
     y = nan_like_out(m, n)
-    bqm.bqm_e4m3_gemm(dev(codes), xq, sc, y)
+    getattr(bqm, E4M3_GEMMS[kernel][0])(dev(codes), xq, sc, y)
     torch.cuda.synchronize()
     return codes, xq_ref, sc_ref, y.cpu().numpy()
 
 
 # K = 128 per LDS stage: one, two, three (K=384) and five (K=640) stages, the
-# odd counts ending after the loop
+# odd counts ending after the loop; every output against its derived bound
+@pytest.mark.parametrize("kernel", ["fp8", "exact"])
 @pytest.mark.parametrize("m,k,n", [(1, 128, 1), (17, 128, 33), (130, 256, 257), (64, 4096, 640),
                                    (200, 1024, 129), (33, 384, 97), (129, 640, 330)])
-def test_e4m3_gemm_matches_oracle(bqm, m, k, n):
-    codes, xq_ref, sc_ref, y = e4m3_gemm_case(bqm, m, k, n, seed=m + k + n)
+def test_e4m3_gemm_matches_oracle(bqm, m, k, n, kernel):
+    codes, xq_ref, sc_ref, y = e4m3_gemm_case(bqm, m, k, n, seed=m + k + n, kernel=kernel)
     y_ref, T = oracle.e4m3_matmul(codes, xq_ref, sc_ref)
-    assert_fold_close(y, y_ref, T, f"e4m3 gemm m={m} k={k} n={n}", tol=e4m3_tolerance(k))
+    worst = assert_fold_close(y, y_ref, T, f"e4m3 {kernel} m={m} k={k} n={n}", tol=E4M3_GEMMS[kernel][1](k))
+    print(f"e4m3 {kernel} m={m} k={k} n={n}: max err/T = {worst:.3e}", flush=True)
 
 
-def test_e4m3_gemm_one_hot(bqm):
+@pytest.mark.parametrize("m,k,n", [(33, 16384, 70), (5, 8192, 300), (257, 512, 1000)])
+def test_e4m3_gemm_exact_long_k_and_ragged(bqm, m, k, n):
+    # the largest k the bounded kernel takes, and ragged tiles at both NT
+    codes, xq_ref, sc_ref, y = e4m3_gemm_case(bqm, m, k, n, seed=7 * m + k + n, kernel="exact")
+    y_ref, T = oracle.e4m3_matmul(codes, xq_ref, sc_ref)
+    worst = assert_fold_close(y, y_ref, T, f"e4m3 exact m={m} k={k} n={n}", tol=exact_bound(k))
+    assert worst <= 1e-5
+
+
+@pytest.mark.parametrize("kernel", ["fp8", "exact"])
+def test_e4m3_gemm_one_hot(bqm, kernel):
     rng = np.random.default_rng(61)
     codes, w_scale = workloads.e4m3_weights(64, 256, rng)
     xq = np.zeros((3, 256), np.uint8)
@@ -351,13 +382,66 @@ def test_e4m3_gemm_one_hot(bqm):
     xq[1, 255] = 0xB8
     xq[2, 128] = 0x38
     sc = np.array([1.0, 1.0, 0.75, 1.0], np.float32)
-    y = bqm.bqm_e4m3_gemm(dev(codes), dev(xq), dev(sc)).cpu().numpy()
+    y = getattr(bqm, E4M3_GEMMS[kernel][0])(dev(codes), dev(xq), dev(sc)).cpu().numpy()
     y_ref, _ = oracle.e4m3_matmul(codes, xq, sc)
     assert np.array_equal(y.astype(np.float64), y_ref)
 
 
-def test_e4m3_full_size_workload(bqm):
+def test_e4m3_gemm_group_truncation_as_measured(bqm):
+    # The datapath the fp8 bound is derived from, seen through the C ABI: with
+    # the weight row all 1.0 and the folded scale 1, a token holding 448 and
+    # 0.140625 in one 8-byte group (k = 0 and 1) loses the small product's
+    # bits below 2^-5 toward zero; in another group (k = 8) or the other lane
+    # half (k = 32) it is added exactly.  The bounded kernel is exact on all.
+    k = 128
+    w = np.full((1, k), 0x38, np.uint8)
+    xq = np.zeros((4, k), np.uint8)
+    xq[:, 0] = 0x7E                       # 448
+    xq[0, 1] = 0x21                       # +0.140625, same group
+    xq[1, 8] = 0x21                       # next group of the lane
+    xq[2, 32] = 0x21                      # the other lane half
+    xq[3, 1] = 0xA1                       # -0.140625, same group
+    sc = np.array([1.0, 1.0, 1.0, 1.0], np.float32)
+    y8 = bqm.bqm_e4m3_gemm(dev(w), dev(xq), dev(sc)).cpu().numpy()[:, 0]
+    ye = bqm.bqm_e4m3_gemm_exact(dev(w), dev(xq), dev(sc)).cpu().numpy()[:, 0]
+    exact = np.array([448.140625, 448.140625, 448.140625, 447.859375], np.float32)
+    assert list(y8) == [448.125, 448.140625, 448.140625, 447.875]
+    assert np.array_equal(ye, exact)
+
+
+@pytest.mark.parametrize("act", ["outliers", "wide"])
+def test_e4m3_gemm_workload_shape_hard_activations(bqm, act):
+    # the FP8 workload's shape (m=512, K=4096, N=20480) with the MMQ
+    # workload's outlier activations (1% scaled by 10) and with activations
+    # spread over 32 binades (most quantize to small or subnormal codes next
+    # to large ones); both kernels on every output, each at its bound, the
+    # observed maxima printed
     m, k, n = 512, 4096, 20480
-    codes, xq_ref, sc_ref, y = e4m3_gemm_case(bqm, m, k, n, seed=0)
-    y_ref, T = oracle.e4m3_matmul(codes, xq_ref, sc_ref)      # every output element
-    assert_fold_close(y, y_ref, T, "e4m3 full size", tol=1e-5)
+    gen = {"outliers": lambda m_, k_, r: workloads.activations(m_, k_, r, outliers=True),
+           "wide": lambda m_, k_, r: workloads.wide_activations(m_, k_, r)}[act]
+    worst = {}
+    y_ref = T = None
+    for kernel in ("fp8", "exact"):
+        codes, xq_ref, sc_ref, y = e4m3_gemm_case(bqm, m, k, n, seed=5, kernel=kernel, act=gen)
+        if y_ref is None:
+            y_ref, T = oracle.e4m3_matmul(codes, xq_ref, sc_ref)
+        worst[kernel] = assert_fold_close(y, y_ref, T, f"e4m3 {kernel} {act}", tol=E4M3_GEMMS[kernel][1](k))
+    print(f"e4m3 workload shape, {act} activations: max err/T fp8 = {worst['fp8']:.3e}, "
+          f"exact = {worst['exact']:.3e}", flush=True)
+    assert worst["exact"] <= 1e-5
+
+
+def test_e4m3_full_size_workload(bqm):
+    # the FP8 workload itself: the bounded kernel within 1e-5 * T by
+    # construction, the fp8 kernel within its bound (and, on this seeded data,
+    # within 1e-5 * T as observed)
+    m, k, n = 512, 4096, 20480
+    y_ref = T = None
+    for kernel in ("exact", "fp8"):
+        codes, xq_ref, sc_ref, y = e4m3_gemm_case(bqm, m, k, n, seed=0, kernel=kernel)
+        if y_ref is None:
+            y_ref, T = oracle.e4m3_matmul(codes, xq_ref, sc_ref)      # every output element
+        worst = assert_fold_close(y, y_ref, T, f"e4m3 {kernel} full size", tol=E4M3_GEMMS[kernel][1](k))
+        print(f"e4m3 {kernel} full size: max err/T = {worst:.3e}", flush=True)
+        if kernel == "exact":
+            assert worst <= 1e-5

@@ -97,6 +97,14 @@ def activations(m: int, k: int, rng: np.random.Generator, outliers: bool = False
     return x
 
 
+def wide_activations(m: int, k: int, rng: np.random.Generator, binades: int = 16) -> np.ndarray:
+    """f32 activations whose magnitudes span 2*binades binades: N(0,1) times
+    2^e with e uniform on [-binades, binades] per value."""
+    x = rng.standard_normal((m, k), dtype=np.float32)
+    e = rng.uniform(-binades, binades, size=(m, k))
+    return (x * np.exp2(e)).astype(np.float32)
+
+
 def e4m3_weights(n: int, k: int, rng: np.random.Generator):
     """e4m3 weights drawn from N(0, 0.02) and stored as codes plus one f32 scale."""
     import torch
