@@ -279,12 +279,12 @@ def test_gemm_full_size_workloads(bqm, n):
     assert_fold_close(y.cpu().numpy(), y_ref, T, f"gemm full n={n}")
 
 
-@pytest.mark.parametrize("k", [256, 1280, 768])
-def test_gemm_tall_tile_stage_counts(bqm, k):
-    # m=512, N=4096 fills the CUs with 128-row tiles (64 column tiles x 4 token
-    # tiles): the tile whose workgroup barrier sits inside the stage.  K=256 is
-    # one stage, K=768 three and K=1280 five (an odd last stage after the
-    # loop); every output against the oracle.
+@pytest.mark.parametrize("k", [256, 1280, 768, 512])
+def test_gemm_iteration_counts(bqm, k):
+    # m=512, N=4096: 64 column tiles x 4 token tiles.  An iteration of the MMQ
+    # covers 256 k (one 128-k stage per k-group): K=256 is one iteration, 512
+    # two, 768 three and 1280 five (the two k-groups' partial sums meet in
+    # LDS after the last); every output against the oracle.
     rng = np.random.default_rng(k)
     m, n = 512, 4096
     w = workloads.q8_0_weights(n, k, rng)
@@ -294,7 +294,7 @@ def test_gemm_tall_tile_stage_counts(bqm, k):
     bqm.bqm_q8_0_gemm(dev(w), xq, xds, y)
     torch.cuda.synchronize()
     y_ref, T = oracle.q8_0_matmul(w, xq_ref, xds_ref, k)
-    assert_fold_close(y.cpu().numpy(), y_ref, T, f"gemm tall tile k={k}")
+    assert_fold_close(y.cpu().numpy(), y_ref, T, f"gemm iterations k={k}")
 
 
 # --------------------------------------------------------------------------- e4m3
