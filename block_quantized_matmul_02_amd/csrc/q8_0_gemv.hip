@@ -501,7 +501,17 @@ template <int M, int PRE, bool QX, bool XR>
 static int launch_sized(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
                         float *y, int k, int n, const GemvGeom &g, int lds_bytes, hipStream_t stream) {
     const int cus = device_cus();
-    const int per_cu = gemv_per_cu<M, PRE, QX, XR>(lds_bytes);
+    int per_cu = gemv_per_cu<M, PRE, QX, XR>(lds_bytes);
+    if (QX) {
+        // Every workgroup of the one-launch step reads and quantizes the whole
+        // f32 activation (16 KiB at K=4096), so at four workgroups per CU a
+        // 17.8 MB weight matrix came with 16 MB of activation reads.  One
+        // workgroup per CU below 48 MB of weights, two above (measured, m=1:
+        // 4096->4096 8.7 -> 6.6 us, 1280->4096 4.7 -> 3.8, 4096->20480 17.0 ->
+        // 16.2, the head unchanged; bitwise the same results).
+        const int cap = (int64_t)n * w_row_bytes < (48ll << 20) ? 1 : 2;
+        if (per_cu > cap) per_cu = cap;
+    }
     int want = (g.n_row_tiles + kGemvWaves - 1) / kGemvWaves;
     int grid = cus * per_cu;
     if (want < grid) grid = want;
