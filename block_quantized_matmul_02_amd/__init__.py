@@ -295,7 +295,8 @@ def bqm_e4m3_nan_count(w, out=None):
 
 
 def bqm_e4m3_blk_quantize(x, xq=None, xs=None):
-    """Per (token, 128-k block) e4m3 quantization of f32 ``x [m, k]`` -> (uint8 ``xq [m, k]``, f32 ``xs [m, k/128]``)."""
+    """Per (token, 128-k block) e4m3 quantization of f32 ``x [m, k]`` -> (uint8 ``xq [m, k]``,
+    f32 ``xs [m, ceil(k/128)]``); k % 16 == 0, the last block short when k % 128 != 0."""
     import torch
 
     m, k = x.shape
@@ -303,24 +304,24 @@ def bqm_e4m3_blk_quantize(x, xq=None, xs=None):
     if xq is None:
         xq = torch.empty((m, k), dtype=torch.uint8, device=x.device)
     if xs is None:
-        xs = torch.empty((m, k // 128), dtype=torch.float32, device=x.device)
+        xs = torch.empty((m, (k + 127) // 128), dtype=torch.float32, device=x.device)
     _check(xq, torch.uint8, "xq", (m, k))
-    _check(xs, torch.float32, "xs", (m, k // 128))
+    _check(xs, torch.float32, "xs", (m, (k + 127) // 128))
     _raise("bqm_e4m3_blk_quantize", lib().bqm_e4m3_blk_quantize(_ptr(x), _ptr(xq), _ptr(xs), m, k, _stream(x)))
     return xq, xs
 
 
 def bqm_e4m3_blk_gemm(w, grid, xq, xs, y=None):
-    """Block-128 FP8 GEMM: e4m3 ``w [n, k]`` with f32 ``grid [ceil(n/128), k/128]``, ``xq``/``xs`` from
+    """Block-128 FP8 GEMM: e4m3 ``w [n, k]`` with f32 ``grid [ceil(n/128), ceil(k/128)]``, ``xq``/``xs`` from
     bqm_e4m3_blk_quantize -> f32 ``y [m, n]``."""
     import torch
 
     n, k = w.shape
     m = xq.shape[0]
     _check(w, torch.uint8, "w")
-    _check(grid, torch.float32, "grid", ((n + 127) // 128, k // 128))
+    _check(grid, torch.float32, "grid", ((n + 127) // 128, (k + 127) // 128))
     _check(xq, torch.uint8, "xq", (m, k))
-    _check(xs, torch.float32, "xs", (m, k // 128))
+    _check(xs, torch.float32, "xs", (m, (k + 127) // 128))
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=w.device)
     _check(y, torch.float32, "y", (m, n))

@@ -44,6 +44,7 @@ EXTRA = {
     "q8_0_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "q8_0_gemv_mma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "e4m3_exact.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "e4m3_blk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -98,14 +98,22 @@ __device__ __forceinline__ float dpp_max16(float v) {
 __device__ __forceinline__ float clamp448b(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
 
 // One 128-value block per 32 lanes (a float4 each), eight blocks per
-// workgroup.  Blocks are numbered t * (k/128) + kb, the order of x and of xs.
+// workgroup.  Blocks are numbered t * kbn + kb (kbn = ceil(k/128)), the order
+// of xs; block kb of token t holds values 128*kb .. min(128*kb + 128, k) - 1
+// of row t (the last block of a row is short when k % 128 != 0; k % 16 == 0,
+// so a lane's float4 is wholly inside or wholly past it).
 __global__ __launch_bounds__(256) void e4m3_blk_quantize_kernel(const float4 *__restrict__ x, int64_t nblocks,
-                                                                unsigned *__restrict__ xq, float *__restrict__ xs) {
+                                                                int k, int kbn, unsigned *__restrict__ xq,
+                                                                float *__restrict__ xs) {
     const int64_t g0 = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
     const bool live = g0 < nblocks;
     const int64_t g = live ? g0 : nblocks - 1;   // past the end: recompute the last block, store nothing
     const int l = threadIdx.x & 31;
-    const float4 v = x[g * 32 + l];
+    const int64_t t = g / kbn;
+    const int kb = (int)(g - t * kbn);
+    const bool in = 128 * kb + 4 * l < k;          // this lane's four values exist
+    const int64_t v4 = (t * k + 128 * kb) / 4 + l;  // its float4 in x (and dword in xq)
+    const float4 v = in ? x[v4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     a = dpp_max16(a);
     a = swap16_max(a);   // lanes l and l^16: the block's 32 lanes
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(256) void e4m3_blk_quantize_kernel(const float4 *__
     const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448b(v.x * mul), clamp448b(v.y * mul), 0, false);
     const int both = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448b(v.z * mul), clamp448b(v.w * mul), lo, true);
     if (live) {
-        xq[g * 32 + l] = (unsigned)both;
+        if (in) xq[v4] = (unsigned)both;
         if (l == 0) xs[g] = s;
     }
 }
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
     const int wm = wave >> 1, wn = wave & 1;
     const int n0 = blockIdx.x * BN;
     const int m0 = blockIdx.y * kB8BM;
-    const int nstage = k / kB8KB;        // = k/128 grid columns
+    const int nstage = (k + kB8KB - 1) / kB8KB;   // = ceil(k/128) grid columns; the last may be short
     const int nbn = (n + 127) / 128;     // grid rows
 
     const __amdgpu_buffer_rsrc_t rA = b8_rsrc(xq + (int64_t)m0 * k, (int64_t)(m - m0) * k);
@@ -184,12 +192,18 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
     const uint32_t soff = (uint32_t)((tid & 127) * nstage * 4);
     auto load_stage = [&](B8Regs<NT> &R, int kc) {
         const int so = kc * kB8KB;
+        // A 16-byte chunk past k (only in a short last stage) would read the
+        // next row: its offset is moved past the resource, so it reads zeros
+        // (0x7FFFFFF0 plus any stage offset stays below 2^32).
+        const bool in = so + 16 * (tid & 7) < k;
 #pragma unroll
         for (int s = 0; s < 2; s++)
-            R.a[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, goff + s * grow64, so, 0));
+            R.a[s] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, in ? goff + s * grow64 : 0x7FFFFFF0u, so, 0));
 #pragma unroll
         for (int s = 0; s < NT; s++)
-            R.b[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, goff + s * grow64, so, 0));
+            R.b[s] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, in ? goff + s * grow64 : 0x7FFFFFF0u, so, 0));
         R.xs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rS, soff, kc * 4, 0));
 #pragma unroll
         for (int j = 0; j < NT; j++) R.g[j] = gcol[j][kc];
@@ -243,14 +257,15 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
             v16f P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, z, 0, 0, 0, 127, 0, 127);
             return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, P, 0, 0, 0, 127, 0, 127);
         };
-        v16f Pc = part(0);
+        // two partial sets, indexed at compile time: tile j+1's MFMAs are
+        // issued before tile j is folded, with no register copies between
+        v16f P[2];
+        P[0] = part(0);
 #pragma unroll
         for (int j = 0; j < NT; j++) {
-            v16f Pn = Pc;
-            if (j + 1 < NT) Pn = part(j + 1 < NT ? j + 1 : j);
+            if (j + 1 < NT) P[(j + 1) & 1] = part(j + 1);
 #pragma unroll
-            for (int v = 0; v < 16; v++) acc[j][v] = __builtin_fmaf(Pc[v], sx[v] * G[j], acc[j][v]);
-            Pc = Pn;
+            for (int v = 0; v < 16; v++) acc[j][v] = __builtin_fmaf(P[j & 1][v], sx[v] * G[j], acc[j][v]);
         }
     };
 
@@ -334,14 +349,15 @@ extern "C" int bqm_e4m3_nan_count(const uint8_t *w, int64_t count, unsigned long
 extern "C" int bqm_e4m3_blk_quantize(const float *x, uint8_t *xq, float *xs, int m, int k, void *stream) {
     using namespace bqm;
     if (!x || !xq || !xs) return BQM_EINVAL;
-    if (m < 1 || k < 128) return BQM_EINVAL;
-    if (k % 128 != 0) return BQM_EUNSUPPORTED;
+    if (m < 1 || k < 16) return BQM_EINVAL;
+    if (k % 16 != 0) return BQM_EUNSUPPORTED;
     if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(xs, 4)) return BQM_EUNSUPPORTED;
-    const int64_t nblocks = (int64_t)m * (k / 128);
+    const int kbn = (k + 127) / 128;
+    const int64_t nblocks = (int64_t)m * kbn;
     const int64_t wgs = (nblocks + 7) / 8;
     if (wgs > 0x7FFFFFFF) return BQM_EUNSUPPORTED;
     hipLaunchKernelGGL(e4m3_blk_quantize_kernel, dim3((unsigned)wgs), dim3(256), 0, as_stream(stream),
-                       reinterpret_cast<const float4 *>(x), nblocks, reinterpret_cast<unsigned *>(xq), xs);
+                       reinterpret_cast<const float4 *>(x), nblocks, k, kbn, reinterpret_cast<unsigned *>(xq), xs);
     return launch_status();
 }
 
@@ -349,8 +365,8 @@ extern "C" int bqm_e4m3_blk_gemm(const uint8_t *w, const float *grid, const uint
                                  int m, int k, int n, void *stream) {
     using namespace bqm;
     if (!w || !grid || !xq || !xs || !y) return BQM_EINVAL;
-    if (m < 1 || k < 128 || n < 1) return BQM_EINVAL;
-    if (k % 128 != 0) return BQM_EUNSUPPORTED;
+    if (m < 1 || k < 16 || n < 1) return BQM_EINVAL;
+    if (k % 16 != 0) return BQM_EUNSUPPORTED;
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(grid, 4) || !aligned(xs, 4) || !aligned(y, 4))
         return BQM_EUNSUPPORTED;
     if ((int64_t)kB8BM * k > 0x7FFFFFF0ll || (int64_t)320 * k > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;

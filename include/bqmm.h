@@ -269,12 +269,15 @@ int bqm_e4m3_nan_count(const uint8_t *w, int64_t count, unsigned long long *nan_
 /*
  * bqm_e4m3_blk_quantize: per (token t, 128-k block kb) e4m3 quantization of
  * the f32 activation with the pages' activation rule amax/448:
- *   amax = max |x[t][128kb .. 128kb+127]|; mul = 448/amax, xs = amax/448 (f32
+ *   amax = max |x[t][128kb .. min(128kb+128, k)-1]| (the last block of a row
+ *   is short when k % 128 != 0); mul = 448/amax, xs = amax/448 (f32
  *   divisions; both 0 when amax is 0); xq = e4m3(clamp(x * mul, +-448)),
  *   round to nearest even, sign of zero kept, NaN codes never produced.
  *   x  : f32 [m][k], 16-byte aligned.      xq : uint8 [m][k] out, 4-byte aligned.
- *   xs : f32 [m][k/128] out, 4-byte aligned.
- *   m >= 1, k >= 128 (else BQM_EINVAL); k % 128 == 0 (else BQM_EUNSUPPORTED).
+ *   xs : f32 [m][ceil(k/128)] out, 4-byte aligned.
+ *   m >= 1, k >= 16 (else BQM_EINVAL); k % 16 == 0 (else BQM_EUNSUPPORTED):
+ *   the pages' gate for this kernel class ("fp8_ffi.rs", try_fp8_blk_mmq:
+ *   in_f a multiple of 16, grid blocks counted by div_ceil(128)).
  * The pages do not show this kernel's activation side; this is the reading
  * that gives one fold per 128-k block on both operands.
  */
@@ -285,10 +288,11 @@ int bqm_e4m3_blk_quantize(const float *x, uint8_t *xq, float *xs, int m, int k, 
  *   sum_{i in kb} e4m3(xq[t][i]) * e4m3(w[r][i]), f32 accumulation, one fold
  *   per 128-k block.
  *   w    : e4m3 codes [n][k], 16-byte aligned, free of NaN codes.
- *   grid : f32 [ceil(n/128)][k/128] row-major, 4-byte aligned.
- *   xq   : e4m3 codes [m][k], 16-byte aligned;  xs : f32 [m][k/128].
+ *   grid : f32 [ceil(n/128)][ceil(k/128)] row-major, 4-byte aligned.
+ *   xq   : e4m3 codes [m][k], 16-byte aligned;  xs : f32 [m][ceil(k/128)].
  *   y    : f32 [m][n] out, fully overwritten.
- *   m, n >= 1, k >= 128 (else BQM_EINVAL); k % 128 == 0 (else BQM_EUNSUPPORTED).
+ *   m, n >= 1, k >= 16 (else BQM_EINVAL); k % 16 == 0 (else BQM_EUNSUPPORTED);
+ *   the last 128-k block is short when k % 128 != 0.
  */
 int bqm_e4m3_blk_gemm(const uint8_t *w, const float *grid, const uint8_t *xq, const float *xs, float *y, int m,
                       int k, int n, void *stream);

@@ -202,8 +202,9 @@ def test_e4m3_blk_validation(L):
     q = L.bqm_e4m3_blk_quantize
     assert q(NUL, B16, C16, 1, 128, NUL) == 1
     assert q(A16, B16, C16, 0, 128, NUL) == 1
-    assert q(A16, B16, C16, 1, 64, NUL) == 1                 # k < 128
-    assert q(A16, B16, C16, 1, 192, NUL) == 2                # k % 128
+    assert q(A16, B16, C16, 1, 0, NUL) == 1                  # k < 16
+    assert q(A16, B16, C16, 1, 8, NUL) == 1
+    assert q(A16, B16, C16, 1, 200, NUL) == 2                # k % 16
     assert q(P(0x100004), B16, C16, 1, 128, NUL) == 2        # x 16-byte alignment
     assert q(A16, MIS2, C16, 1, 128, NUL) == 2
     g = L.bqm_e4m3_blk_gemm
@@ -211,7 +212,8 @@ def test_e4m3_blk_validation(L):
     assert g(A16, NUL, C16, D16, A16, 1, 128, 8, NUL) == 1
     assert g(A16, B16, C16, D16, NUL, 1, 128, 8, NUL) == 1
     assert g(A16, B16, C16, D16, A16, 1, 128, 0, NUL) == 1
-    assert g(A16, B16, C16, D16, A16, 1, 256 + 64, 8, NUL) == 2
+    assert g(A16, B16, C16, D16, A16, 1, 8, 8, NUL) == 1      # k < 16
+    assert g(A16, B16, C16, D16, A16, 1, 256 + 8, 8, NUL) == 2        # k % 16
     assert g(MIS2, B16, C16, D16, A16, 1, 128, 8, NUL) == 2
     assert g(A16, B16, P(0x300004), D16, A16, 1, 128, 8, NUL) == 2   # xq 16-byte alignment
 

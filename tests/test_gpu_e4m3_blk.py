@@ -25,7 +25,7 @@ DEV = "cuda:0"
 
 
 def tolerance(k):
-    return 7 * 2.0 ** -13 + (k // 128 + 18) * 2.0 ** -24
+    return 7 * 2.0 ** -13 + ((k + 127) // 128 + 18) * 2.0 ** -24
 
 
 @pytest.fixture(scope="module")
@@ -80,12 +80,14 @@ def test_nan_count_clean_weight_and_planted_codes(bqm):
 # --------------------------------------------------------------------------- quantization
 
 
-@pytest.mark.parametrize("m,k", [(1, 128), (3, 256), (130, 4096), (512, 4096), (7, 8192)])
+# k % 128 != 0 (the pages' gate is k % 16): the last block of each row is short
+@pytest.mark.parametrize("m,k", [(1, 128), (3, 256), (130, 4096), (512, 4096), (7, 8192),
+                                 (2, 16), (3, 48), (5, 208), (9, 4112), (4, 2064)])
 def test_blk_quantize_bit_exact(bqm, m, k):
     rng = np.random.default_rng(m * 7 + k)
     x = workloads.activations(m, k, rng, outliers=True)
-    x[0, :128] = 0.0                                        # an all-zero block
-    x[-1, -128:] *= np.float32(1e-30)                       # a block of tiny values
+    x[0, :min(k, 128)] = 0.0                                # an all-zero block
+    x[-1, -(k - 128 * ((k - 1) // 128)):] *= np.float32(1e-30)   # the (possibly short) last block, tiny values
     x[-1, 5] = -0.0
     xq, xs = bqm.bqm_e4m3_blk_quantize(dev(x))
     torch.cuda.synchronize()
@@ -111,7 +113,8 @@ def gemm_case(bqm, m, k, n, seed):
 # 40000) NT=3, (256, 256, 30000) NT=4 on 256 compute units, the full-size
 # workload NT=5
 @pytest.mark.parametrize("m,k,n", [(1, 128, 1), (17, 256, 33), (130, 512, 300), (64, 4096, 640), (200, 1024, 129),
-                                   (3, 8192, 70), (256, 384, 1000), (128, 128, 40000), (256, 256, 30000)])
+                                   (3, 8192, 70), (256, 384, 1000), (128, 128, 40000), (256, 256, 30000),
+                                   (5, 16, 70), (17, 208, 300), (33, 4112, 257), (64, 2064, 640), (130, 144, 1000)])
 def test_blk_gemm_matches_oracle(bqm, m, k, n):
     w, grid, xq, xs, y = gemm_case(bqm, m, k, n, seed=m + k + n)
     y_ref, T = oracle.e4m3_blk_matmul(w, grid, xq, xs)
@@ -132,6 +135,22 @@ def test_blk_gemm_one_hot_exact(bqm):
     rb = np.arange(n) // 128
     for t, c in enumerate(cols):
         assert np.array_equal(y[t], grid[rb, c // 128] * dec[:, c])
+
+
+@pytest.mark.parametrize("m,k,n", [(9, 4112, 385), (200, 2064, 129)])
+def test_blk_ragged_k_device_chain(bqm, m, k, n):
+    # a short last 128-k block through the device quantizer and the GEMM
+    rng = np.random.default_rng(k + n)
+    w, grid = workloads.e4m3_blk_weights(n, k, rng)
+    x = workloads.activations(m, k, rng, outliers=True)
+    xq, xs = bqm.bqm_e4m3_blk_quantize(dev(x))
+    y = bqm.bqm_e4m3_blk_gemm(dev(w), dev(grid), xq, xs)
+    torch.cuda.synchronize()
+    xq_ref, xs_ref = oracle.e4m3_blk_quantize(x)
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), xs_ref.view(np.uint32))
+    y_ref, T = oracle.e4m3_blk_matmul(w, grid, xq_ref, xs_ref)
+    check(y.cpu().numpy(), y_ref, T, f"blk ragged chain m={m} k={k} n={n}", tolerance(k))
 
 
 def test_blk_full_size_prefill(bqm):
