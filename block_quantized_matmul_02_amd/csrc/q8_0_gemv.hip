@@ -506,10 +506,12 @@ static int launch_sized(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq,
         // Every workgroup of the one-launch step reads and quantizes the whole
         // f32 activation (16 KiB at K=4096), so at four workgroups per CU a
         // 17.8 MB weight matrix came with 16 MB of activation reads.  One
-        // workgroup per CU below 48 MB of weights, two above (measured, m=1:
-        // 4096->4096 8.7 -> 6.6 us, 1280->4096 4.7 -> 3.8, 4096->20480 17.0 ->
-        // 16.2, the head unchanged; bitwise the same results).
-        const int cap = (int64_t)n * w_row_bytes < (48ll << 20) ? 1 : 2;
+        // workgroup per CU below 48 MB of weights, two below 128 MB, no cap
+        // above (measured, m=1: 4096->4096 8.7 -> 6.6 us, 1280->4096 4.7 ->
+        // 3.8, 4096->20480 17.0 -> 16.2; the 280 MB head runs 0.5 us faster
+        // with four; bitwise the same results).
+        const int64_t wbytes = (int64_t)n * w_row_bytes;
+        const int cap = wbytes < (48ll << 20) ? 1 : wbytes < (128ll << 20) ? 2 : 4;
         if (per_cu > cap) per_cu = cap;
     }
     int want = (g.n_row_tiles + kGemvWaves - 1) / kGemvWaves;
