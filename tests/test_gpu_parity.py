@@ -281,10 +281,10 @@ def test_gemm_full_size_workloads(bqm, n):
 
 @pytest.mark.parametrize("k", [256, 1280, 768, 512])
 def test_gemm_iteration_counts(bqm, k):
-    # m=512, N=4096: 64 column tiles x 4 token tiles.  An iteration of the MMQ
-    # covers 256 k (one 128-k stage per k-group): K=256 is one iteration, 512
-    # two, 768 three and 1280 five (the two k-groups' partial sums meet in
-    # LDS after the last); every output against the oracle.
+    # m=512, N=4096: 64 column tiles x 4 token tiles.  The MMQ's loop covers
+    # two 128-k stages per trip: K=256 is one trip (prologue and both LDS
+    # buffers only), 512 two, 768 three and 1280 five; every output against
+    # the oracle.
     rng = np.random.default_rng(k)
     m, n = 512, 4096
     w = workloads.q8_0_weights(n, k, rng)
