@@ -18,8 +18,10 @@ group sums are then accumulated in f32, and the fold adds at most
 
     |y - y_ref| <= (7 * 2^-13 + (K/32 + 4) * 2^-24) * T,
 
-T the sum of the magnitudes of every product term (8.5e-4 * T; the full-range
-"wide" bytes reach 1.2e-4 * T, the mid-exponent bytes 7e-8 * T).  Exactly 0
+T the sum of the magnitudes of every product term (8.5e-4 * T at K = 4096;
+the cases below print their maxima: the full-range "wide" bytes reach about
+7e-5 * T at K = 256 and 2.3e-5 * T at 512 x 5120 x 5120, the mid-exponent bytes
+below 1e-7 * T).  Exactly 0
 where T is 0.  The int8 arm is bqm_q8_0_gemm itself, covered by the MMQ's
 parity tests.
 """
