@@ -75,8 +75,30 @@ def recorded_traffic():
         return None
 
 
-def timed_loop(torch, stream, steps, fns):
-    """Time ``steps`` passes of ``fns`` (a list of (name, callable)).
+class region:
+    """A named marker range around GPU work (torch's range markers, roctx on
+    ROCm), so a profiler run with ``--marker-trace --kernel-rename`` names each
+    kernel dispatch by the workload and call it belongs to; it costs nothing
+    without a profiler."""
+
+    def __init__(self, torch, name):
+        self.torch, self.name = torch, name
+
+    def __enter__(self):
+        if self.name:
+            self.torch.cuda.nvtx.range_push(self.name)
+        return self
+
+    def __exit__(self, *exc):
+        if self.name:
+            self.torch.cuda.nvtx.range_pop()
+        return False
+
+
+def timed_loop(torch, stream, steps, fns, label=None):
+    """Time ``steps`` passes of ``fns`` (a list of (name, callable)); with a
+    ``label`` every dispatch runs inside the marker range "label: name" (the
+    whole loop: "label: step").
 
     The launches are captured once into a HIP graph (torch.cuda.graph) and
     replayed, so host-side launch overhead is out of the measurement: the
@@ -123,8 +145,13 @@ def timed_loop(torch, stream, steps, fns):
 
     # the step loop: exactly `steps` passes, timed once; each kernel: the
     # median of 9 replays of `steps` back-to-back launches
-    total_ms = replay_ms(capture([fn for _, fn in fns]))
-    per = {name: replay_ms(capture([fn]), reps=9) / steps for name, fn in fns}
+    tag = (lambda what: f"{label}: {what}") if label else (lambda what: None)
+    with region(torch, tag("step")):
+        total_ms = replay_ms(capture([fn for _, fn in fns]))
+    per = {}
+    for name, fn in fns:
+        with region(torch, tag(name)):
+            per[name] = replay_ms(capture([fn]), reps=9) / steps
     return total_ms, per
 
 
@@ -316,13 +343,15 @@ def main():
         # runs the GEMV (bitwise equal to the two-launch path timed below)
         fns = [("gemv_f32", lambda s: bqm.bqm_q8_0_gemv_f32(ws[s % ROTATE], x, y))]
         log("[bench] gemv warmup")
-        timed_loop(torch, stream, args.warmup, fns)
+        hl = f"Q8_0 decode head m=1 {k}->{n}, one launch"
+        timed_loop(torch, stream, args.warmup, fns, hl)
         log("[bench] gemv timed")
-        total_ms, per = timed_loop(torch, stream, args.steps, fns)
+        total_ms, per = timed_loop(torch, stream, args.steps, fns, hl)
         fns2 = [("quantize", lambda s: bqm.bqm_q8_1_quantize(x, xq, xds)),
                 ("gemv", lambda s: bqm.bqm_q8_0_gemv(ws[s % ROTATE], xq, xds, y))]
-        timed_loop(torch, stream, args.warmup, fns2)
-        total2_ms, per2 = timed_loop(torch, stream, args.steps, fns2)
+        hl2 = f"Q8_0 decode head m=1 {k}->{n}, two launches"
+        timed_loop(torch, stream, args.warmup, fns2, hl2)
+        total2_ms, per2 = timed_loop(torch, stream, args.steps, fns2, hl2)
         step_bytes = n * (k // 32) * 34 + m * k * 4 + m * n * 4       # weights + f32 activation + y
         ms_step = total_ms / args.steps
         achieved = step_bytes / (per["gemv_f32"] * 1e-3) / 1e9
@@ -365,13 +394,15 @@ def main():
                 row = {}
                 if m <= 2 and m * k <= 8192:          # the one-launch step is for decode
                     fns = [("gemv_f32", lambda s: bqm.bqm_q8_0_gemv_f32(ws[s % copies], x, y))]
-                    timed_loop(torch, stream, args.warmup, fns)
-                    _, per = timed_loop(torch, stream, args.steps, fns)
+                    sl = f"Q8_0 sweep m={m} {k}->{n}, one launch"
+                    timed_loop(torch, stream, args.warmup, fns, sl)
+                    _, per = timed_loop(torch, stream, args.steps, fns, sl)
                     row["one_launch_us"] = round(per["gemv_f32"] * 1e3, 2)
                 fns2 = [("quantize", lambda s: bqm.bqm_q8_1_quantize(x, xq, xds)),
                         ("gemv", lambda s: bqm.bqm_q8_0_gemv(ws[s % copies], xq, xds, y))]
-                timed_loop(torch, stream, args.warmup, fns2)
-                t2, per2 = timed_loop(torch, stream, args.steps, fns2)
+                sl2 = f"Q8_0 sweep m={m} {k}->{n}, two launches"
+                timed_loop(torch, stream, args.warmup, fns2, sl2)
+                t2, per2 = timed_loop(torch, stream, args.steps, fns2, sl2)
                 row["two_launch_step_us"] = round(t2 / args.steps * 1e3, 2)
                 row["two_launch_gemv_us"] = round(per2["gemv"] * 1e3, 2)
                 best = min(row.get("one_launch_us", 1e9), row["two_launch_step_us"])
@@ -407,8 +438,9 @@ def main():
             y = torch.empty((m, n), dtype=torch.float32, device=dev)
             fns = [("quantize", lambda s: bqm.bqm_q8_1_quantize(x, xq, xds)),
                    ("gemm", lambda s: bqm.bqm_q8_0_gemm(ws[s % nc], xq, xds, y))]
-            timed_loop(torch, stream, args.warmup, fns)
-            total_ms, per = timed_loop(torch, stream, args.steps, fns)
+            ml = f"MMQ m={m} {k}->{n}"
+            timed_loop(torch, stream, args.warmup, fns, ml)
+            total_ms, per = timed_loop(torch, stream, args.steps, fns, ml)
             ops = 2.0 * m * n * k
             tops = ops / (per["gemm"] * 1e-3) / 1e12
             mmq[str(n)] = {"workload": f"MMQ GEMM m=512, K=4096, N={n}, Q8_0 x q8_1 (1% outliers x10)",
@@ -434,12 +466,13 @@ def main():
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         fns = [("quantize", lambda s: bqm.bqm_e4m3_quantize_amax(x, w_scale, xq8, sc)),
                ("gemm", lambda s: bqm.bqm_e4m3_gemm(ws[s % nc], xq8, sc, y))]
-        timed_loop(torch, stream, args.warmup, fns)
-        total_ms, per = timed_loop(torch, stream, args.steps, fns)
+        el = f"e4m3 GEMM m={m} {k}->{n}"
+        timed_loop(torch, stream, args.warmup, fns, el)
+        total_ms, per = timed_loop(torch, stream, args.steps, fns, el)
         # the bounded kernel (fp16 matrix cores, within 1e-5 * sum|terms| for any data)
         fx = [("gemm_exact", lambda s: bqm.bqm_e4m3_gemm_exact(ws[s % nc], xq8, sc, y))]
-        timed_loop(torch, stream, args.warmup, fx)
-        _, perx = timed_loop(torch, stream, args.steps, fx)
+        timed_loop(torch, stream, args.warmup, fx, el)
+        _, perx = timed_loop(torch, stream, args.steps, fx, el)
         ops = 2.0 * m * n * k
         tf = ops / (per["gemm"] * 1e-3) / 1e12
         tfx = ops / (perx["gemm_exact"] * 1e-3) / 1e12
@@ -466,8 +499,9 @@ def main():
             x = torch.from_numpy(workloads.activations(m, k, rng)).to(dev)
             y = torch.empty((m, n), dtype=torch.float32, device=dev)
             fns = [("gemv", lambda s: bqm.bqm_e4m3_gemv(ws[s % ROTATE], x, w_scale, y))]
-            timed_loop(torch, stream, args.warmup, fns)
-            _, per = timed_loop(torch, stream, args.steps, fns)
+            gl = f"e4m3 GEMV m={m} {k}->{n}"
+            timed_loop(torch, stream, args.warmup, fns, gl)
+            _, per = timed_loop(torch, stream, args.steps, fns, gl)
             byts = n * k + m * k * 4 + m * n * 4
             gbs = byts / (per["gemv"] * 1e-3) / 1e9
             e8[f"m{m}"] = {"workload": f"e4m3 decode GEMV m={m}, K=4096, N=64448, raw e4m3 weights, f32 activations",
@@ -491,11 +525,12 @@ def main():
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         fns = [("cvt", lambda s: bqm.bqm_f16_cvt(x, x16)),
                ("gemm", lambda s: bqm.bqm_f16_gemm(w16s[s % nc], x16, y))]
-        timed_loop(torch, stream, args.warmup, fns)
-        total_ms, per = timed_loop(torch, stream, args.steps, fns)
+        fl = f"fp16 mirror m={m} {k}->{n}"
+        timed_loop(torch, stream, args.warmup, fns, fl)
+        total_ms, per = timed_loop(torch, stream, args.steps, fns, fl)
         dq = [("dequant", lambda s: bqm.bqm_q8_0_dequant_f16(wq, k, w16s[s % nc]))]
-        timed_loop(torch, stream, 2, dq)
-        _, per_dq = timed_loop(torch, stream, args.steps, dq)
+        timed_loop(torch, stream, 2, dq, fl)
+        _, per_dq = timed_loop(torch, stream, args.steps, dq, fl)
         ops = 2.0 * m * n * k
         tf = ops / (per["gemm"] * 1e-3) / 1e12
         dq_bytes = q8_0_bytes(0, k, n) + 2 * n * k
@@ -524,12 +559,13 @@ def main():
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
         fns = [("quantize", lambda s: bqm.bqm_e4m3_blk_quantize(x, xq8, xs)),
                ("gemm", lambda s: bqm.bqm_e4m3_blk_gemm(ws[s % nc], grid, xq8, xs, y))]
-        timed_loop(torch, stream, args.warmup, fns)
-        total_ms, per = timed_loop(torch, stream, args.steps, fns)
+        bl = f"block-128 FP8 m={m} {k}->{n}"
+        timed_loop(torch, stream, args.warmup, fns, bl)
+        total_ms, per = timed_loop(torch, stream, args.steps, fns, bl)
         cnt = torch.empty(1, dtype=torch.int64, device=dev)
         scan = [("nan_scan", lambda s: bqm.bqm_e4m3_nan_count(ws[s % nc], cnt))]
-        timed_loop(torch, stream, 2, scan)
-        _, per_scan = timed_loop(torch, stream, args.steps, scan)
+        timed_loop(torch, stream, 2, scan, bl)
+        _, per_scan = timed_loop(torch, stream, args.steps, scan, bl)
         ops = 2.0 * m * n * k
         tf = ops / (per["gemm"] * 1e-3) / 1e12
         out["e4m3_blk_m512"] = {
@@ -569,11 +605,12 @@ def main():
                     for _ in range(reps):
                         for arm in ("f32", "s32"):           # interleaved inside each rep
                             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                            e0.record(stream)
-                            for _ in range(batch):
-                                arms[arm]()
-                            e1.record(stream)
-                            e1.synchronize()
+                            with region(torch, f"instrument {sheet} {dist} m={m} {k}->{n}: {arm}"):
+                                e0.record(stream)
+                                for _ in range(batch):
+                                    arms[arm]()
+                                e1.record(stream)
+                                e1.synchronize()
                             t[arm].append(e0.elapsed_time(e1) / batch)
                     a, b = sorted(t["f32"])[reps // 2], sorted(t["s32"])[reps // 2]
                     ratio = a / b

@@ -22,14 +22,20 @@
 //    two stages ahead in registers; NT (2..5) chosen per shape so the tiles
 //    fill whole rounds of the CUs (m=512, N=20480: NT=5, 256 tiles).
 //  * Per stage and 32x32 tile a wave runs two v_mfma_scale_f32_32x32x64_f8f6f4
-//    (unit E8M0 scales) into a block partial P started at zero and folds it
-//    at once, acc += P * (xs[t] * g), two VALU ops per output element.  Two
-//    partials are live, so tile j+1's MFMAs are issued before tile j is
-//    folded and the fold runs under them (NT=5: 232 VGPRs; with one partial
-//    register set the next MFMAs waited for the fold).  g is one
-//    scalar per 32-column tile (a 32-aligned tile never straddles a 128-row
-//    block of the grid), read with scalar loads one stage ahead; the 128
-//    token scales of the stage go through LDS with the operand tiles.
+//    (unit E8M0 scales) into a block partial P started at zero and folds it,
+//    acc += P * (xs[t] * g).  g is one scalar per 32-column tile (a 32-aligned
+//    tile never straddles a 128-row block of the grid), read with scalar
+//    loads one stage ahead; the 128 token scales of the stage go through LDS
+//    with the operand tiles.
+//  * NT >= 3: the weight tile is the MFMA's A operand, so the partial is
+//    [weight row][token] and a lane's 16 outputs share one token, hence one
+//    scale xs[t] * g: one multiply and 16 fma per tile and stage.  Three
+//    partials rotate, so a tile is folded while the next two tiles' MFMAs
+//    run (a fold that reads MFMA results issued just before it barely
+//    overlaps the matrix cores).  Interleaved on one box at m=512, K=4096,
+//    N=20480: 68.4 us against 73.1 with [token][row] partials, two in flight
+//    and 16 multiplies per tile; bitwise the same results.
+//  * NT = 2 keeps the [token][row] layout with two partials (faster there).
 #include "bqmm_internal.h"
 
 namespace bqm {
@@ -164,6 +170,11 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
                                                                  const float *__restrict__ xs,
                                                                  float *__restrict__ y, int m, int k, int n) {
     constexpr int BN = 64 * NT;
+    // NT >= 3: partials in [weight row][token] layout, three in flight (see
+    // compute_stage); NT = 2 keeps [token][weight row] and two partials,
+    // which measured faster there (33.4 against 36.3 us at m=512, K=4096,
+    // N=4096; both bitwise the same).
+    constexpr bool kSwap = NT >= 3;
     __shared__ __attribute__((aligned(16))) B8Stage<NT> st[2];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -240,32 +251,61 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
             return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         };
         const v8i a0 = ld8(pa), a1 = ld8(pa + 64);
-        // token scales of the 16 output rows of this lane: rows
-        // wm*32 + 8*(v/4) + 4*khalf + v%4, four consecutive per float4
-        float sx[16];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float4 q = *reinterpret_cast<const float4 *>(S.xs + wm * 32 + 8 * i + 4 * khalf);
-            sx[4 * i + 0] = q.x;
-            sx[4 * i + 1] = q.y;
-            sx[4 * i + 2] = q.z;
-            sx[4 * i + 3] = q.w;
-        }
         const v16f z = {0};
-        auto part = [&](int j) {
-            const v8i b0 = ld8(pb + j * 32 * kB8RowStride), b1 = ld8(pb + j * 32 * kB8RowStride + 64);
-            v16f P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, z, 0, 0, 0, 127, 0, 127);
-            return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, P, 0, 0, 0, 127, 0, 127);
-        };
-        // two partial sets, indexed at compile time: tile j+1's MFMAs are
-        // issued before tile j is folded, with no register copies between
-        v16f P[2];
-        P[0] = part(0);
+        if constexpr (kSwap) {
+            // The weight tile is the MFMA's A operand and the tokens its B
+            // operand, so the partial is [weight row][token]: lane l holds
+            // token wm*32 + l%32 and weight rows 8*(v/4) + 4*khalf + v%4 of
+            // the tile, and the scale xs[t] * g of its 16 outputs is one value
+            // (one multiply and 16 fma per tile instead of 16 of each).
+            const float sxt = S.xs[wm * 32 + (lane & 31)];
+            auto part = [&](int j) {
+                const v8i b0 = ld8(pb + j * 32 * kB8RowStride), b1 = ld8(pb + j * 32 * kB8RowStride + 64);
+                v16f P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a0, z, 0, 0, 0, 127, 0, 127);
+                return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a1, P, 0, 0, 0, 127, 0, 127);
+            };
+            // Three partial sets, indexed at compile time: tiles j+1 and j+2
+            // are on the matrix cores while tile j is folded.  A fold that
+            // reads the MFMA results issued just before it barely overlaps
+            // them (measured: 21% of the fold's time hidden, 62% two tiles
+            // behind).
+            v16f P[3];
+            P[0] = part(0);
+            P[1] = part(1);
 #pragma unroll
-        for (int j = 0; j < NT; j++) {
-            if (j + 1 < NT) P[(j + 1) & 1] = part(j + 1);
+            for (int j = 0; j < NT; j++) {
+                if (j + 2 < NT) P[(j + 2) % 3] = part(j + 2);
+                const float sj = sxt * G[j];
 #pragma unroll
-            for (int v = 0; v < 16; v++) acc[j][v] = __builtin_fmaf(P[j & 1][v], sx[v] * G[j], acc[j][v]);
+                for (int v = 0; v < 16; v++) acc[j][v] = __builtin_fmaf(P[j % 3][v], sj, acc[j][v]);
+            }
+        } else {
+            // token scales of the 16 output rows of this lane: rows
+            // wm*32 + 8*(v/4) + 4*khalf + v%4, four consecutive per float4
+            float sx[16];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float4 q = *reinterpret_cast<const float4 *>(S.xs + wm * 32 + 8 * i + 4 * khalf);
+                sx[4 * i + 0] = q.x;
+                sx[4 * i + 1] = q.y;
+                sx[4 * i + 2] = q.z;
+                sx[4 * i + 3] = q.w;
+            }
+            auto part = [&](int j) {
+                const v8i b0 = ld8(pb + j * 32 * kB8RowStride), b1 = ld8(pb + j * 32 * kB8RowStride + 64);
+                v16f P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, z, 0, 0, 0, 127, 0, 127);
+                return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, P, 0, 0, 0, 127, 0, 127);
+            };
+            // two partial sets, indexed at compile time: tile j+1's MFMAs are
+            // issued before tile j is folded, with no register copies between
+            v16f P[2];
+            P[0] = part(0);
+#pragma unroll
+            for (int j = 0; j < NT; j++) {
+                if (j + 1 < NT) P[(j + 1) & 1] = part(j + 1);
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[j][v] = __builtin_fmaf(P[j & 1][v], sx[v] * G[j], acc[j][v]);
+            }
         }
     };
 
@@ -289,14 +329,40 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
     }
     if (kc < nstage) compute_stage(st[0], G0);
 
+    if constexpr (kSwap) {
+        // Output (token t, weight rows r..r+3) as one 16-byte store where the
+        // four rows are in range and the address 16-byte aligned, else one
+        // float each.
+        const int t = m0 + wm * 32 + (lane & 31);
+        if (t < m) {
+            float *yt = y + (int64_t)t * n;
+            const bool vec = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
 #pragma unroll
-    for (int j = 0; j < NT; j++) {
-        const int col = n0 + wn * 32 * NT + j * 32 + (lane & 31);
-        if (col >= n) continue;
+            for (int j = 0; j < NT; j++) {
 #pragma unroll
-        for (int v = 0; v < 16; v++) {
-            const int row = m0 + wm * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
-            if (row < m) y[(int64_t)row * n + col] = acc[j][v];
+                for (int g = 0; g < 4; g++) {
+                    const int r = n0 + wn * 32 * NT + j * 32 + 8 * g + 4 * khalf;
+                    if (vec && r + 3 < n) {
+                        *reinterpret_cast<float4 *>(yt + r) =
+                            make_float4(acc[j][4 * g], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            if (r + i < n) yt[r + i] = acc[j][4 * g + i];
+                    }
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NT; j++) {
+            const int col = n0 + wn * 32 * NT + j * 32 + (lane & 31);
+            if (col >= n) continue;
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int row = m0 + wm * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+                if (row < m) y[(int64_t)row * n + col] = acc[j][v];
+            }
         }
     }
 }
