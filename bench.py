@@ -298,8 +298,9 @@ def main():
         print(json.dumps(cpu_oracle_legs(single=True)), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              "(the path shards along N with no exchange; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the path would shard "
+              "along N (weight rows) with no exchange, and only the one-GPU share is built and timed",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
