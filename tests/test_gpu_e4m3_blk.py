@@ -121,6 +121,25 @@ def test_blk_gemm_matches_oracle(bqm, m, k, n):
     check(y, y_ref, T, f"blk gemm m={m} k={k} n={n}", tolerance(k))
 
 
+# NT >= 3 stores four output rows of a token with one 16-byte store when n is
+# a multiple of 4 and y is 16-byte aligned, else one float at a time: both
+# paths, with a ragged last tile (NT=3 and NT=4 on 256 compute units).
+@pytest.mark.parametrize("m,k,n,offset", [(128, 128, 40002, 0), (128, 128, 40000, 1), (256, 256, 30001, 0),
+                                          (256, 256, 30000, 3)])
+def test_blk_gemm_store_paths(bqm, m, k, n, offset):
+    rng = np.random.default_rng(n + offset)
+    w, grid = workloads.e4m3_blk_weights(n, k, rng)
+    xq, xs = oracle.e4m3_blk_quantize(workloads.activations(m, k, rng, outliers=True))
+    buf = torch.full((m * n + offset + 4,), float("nan"), dtype=torch.float32, device=DEV)
+    y = buf[offset:offset + m * n].view(m, n)
+    bqm.bqm_e4m3_blk_gemm(dev(w), dev(grid), dev(xq), dev(xs), y)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(np.isnan(b[:offset])) and np.all(np.isnan(b[offset + m * n:])), "writes outside y"
+    y_ref, T = oracle.e4m3_blk_matmul(w, grid, xq, xs)
+    check(y.cpu().numpy(), y_ref, T, f"blk gemm store paths m={m} k={k} n={n} offset={offset}", tolerance(k))
+
+
 def test_blk_gemm_one_hot_exact(bqm):
     # one activation code 1.0 per token with xs = 1: y = f32(grid * dec(w)), one rounding
     n, k = 300, 384
