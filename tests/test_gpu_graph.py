@@ -1,7 +1,7 @@
-"""The entry points inside a captured HIP graph (how bench.py times them, and
+"""Every entry point inside a captured HIP graph (how bench.py times them, and
 how an engine's decode step would run them): each replay must reproduce the
 eager launches bit for bit, with eager work and synchronisations between the
-replays."""
+replays (the NaN count's zeroing kernel included)."""
 import numpy as np
 import pytest
 
@@ -32,6 +32,12 @@ def test_graph_replays_match_eager(bqm):
     x64 = torch.from_numpy(workloads.activations(64, k, rng, outliers=True)).to(dev)
     codes, ws = workloads.e4m3_weights(320, k, rng)
     w8 = torch.from_numpy(codes).to(dev)
+    bcodes, bgrid = workloads.e4m3_blk_weights(700, k, rng)
+    wb = torch.from_numpy(bcodes).to(dev)
+    gb = torch.from_numpy(bgrid).to(dev)
+    wa = torch.from_numpy(workloads.accprobe_weights(300, k, rng, "wide")).to(dev)
+    aq, ad = workloads.accprobe_activations(64, k, rng, "wide")
+    aq, ad = torch.from_numpy(aq).to(dev), torch.from_numpy(ad).to(dev)
 
     def bufs():
         return {
@@ -47,6 +53,18 @@ def test_graph_replays_match_eager(bqm):
             "q8": torch.empty((64, k), dtype=torch.uint8, device=dev),
             "sc": torch.empty(4, dtype=torch.float32, device=dev),
             "y8": torch.empty((64, 320), dtype=torch.float32, device=dev),
+            "y8x": torch.empty((64, 320), dtype=torch.float32, device=dev),
+            "yf": torch.empty((1, 1000), dtype=torch.float32, device=dev),
+            "ye1": torch.empty((1, 320), dtype=torch.float32, device=dev),
+            "ye9": torch.empty((9, 320), dtype=torch.float32, device=dev),
+            "nan": torch.empty(1, dtype=torch.int64, device=dev),
+            "bq": torch.empty((64, k), dtype=torch.uint8, device=dev),
+            "bs": torch.empty((64, k // 128), dtype=torch.float32, device=dev),
+            "yb": torch.empty((64, 700), dtype=torch.float32, device=dev),
+            "w16": torch.empty((1000, k), dtype=torch.float16, device=dev),
+            "x16": torch.empty((64, k), dtype=torch.float16, device=dev),
+            "y16": torch.empty((64, 1000), dtype=torch.float32, device=dev),
+            "ya": torch.empty((64, 300), dtype=torch.float32, device=dev),
         }
 
     def step(b):
@@ -58,6 +76,17 @@ def test_graph_replays_match_eager(bqm):
         bqm.bqm_q8_0_gemm(w, b["xq64"], b["xd64"], b["y64"])
         bqm.bqm_e4m3_quantize_amax(x64, ws, b["q8"], b["sc"])
         bqm.bqm_e4m3_gemm(w8, b["q8"], b["sc"], b["y8"])
+        bqm.bqm_e4m3_gemm_exact(w8, b["q8"], b["sc"], b["y8x"])
+        bqm.bqm_q8_0_gemv_f32(w, x1, b["yf"])
+        bqm.bqm_e4m3_gemv(w8, x1, ws, b["ye1"])
+        bqm.bqm_e4m3_gemv(w8, x9, ws, b["ye9"])
+        bqm.bqm_e4m3_nan_count(wb, b["nan"])
+        bqm.bqm_e4m3_blk_quantize(x64, b["bq"], b["bs"])
+        bqm.bqm_e4m3_blk_gemm(wb, gb, b["bq"], b["bs"], b["yb"])
+        bqm.bqm_q8_0_dequant_f16(w, k, b["w16"])
+        bqm.bqm_f16_cvt(x64, b["x16"])
+        bqm.bqm_f16_gemm(b["w16"], b["x16"], b["y16"])
+        bqm.bqm_q8_0_gemm_f8acc(wa, aq, ad, b["ya"])
 
     eager = bufs()
     step(eager)
