@@ -11,16 +11,25 @@
 //    gives the int32 block sums S of a 32x32 output tile.
 //  * The fold is per output element and block: acc = fma(float(S),
 //    d_x * d_w, acc).  The scale products come from the matrix core (see
-//    scale2), which leaves two VALU ops per element and block.  Measured in
-//    a register-only probe at four waves per SIMD (cycles of the 2.4 GHz
-//    reference clock per 32x32 tile and block): the fold's 32 VALU ops take
-//    86 (the same with the convert replaced by a subtract of a biased MFMA
-//    result), the int8 MFMA with the dependent fold 115, and with the
-//    scale-product MFMA 136, the floor of this design (73 us at m=512,
-//    K=4096, N=20480).  Two waves per SIMD give nearly the same rates.
-//  * Workgroup: 8 waves over a 128-token x 64-row output tile (4 x 2 wave
-//    tiles of 32x32), two workgroups per CU (four waves per SIMD, at most 128
-//    VGPRs each).  Each workgroup runs the whole k loop in 128-k stages; the
+//    scale2), which leaves two VALU ops per element and block.  Per 32x32
+//    tile and block that is 32 cycles of int8 MFMA, 32 of scale-product MFMA
+//    (64 per block pair) and 32 VALU instructions of 4 cycles each (wave64
+//    on 16 lanes; no packed f32).  Counters of the full kernels at m=512,
+//    K=4096, N=20480: VALU busy is exactly 4 cycles per VALU instruction and
+//    the matrix core is busy exactly its instructions' cycles.  For the wide
+//    tile the two add up to 98% of the SQ busy cycles (per shader engine), so
+//    its SIMDs hardly ever wait and the fold is the bound; those launches ran
+//    at about 1.8 GHz (SQ_BUSY_CYCLES over the 32 shader engines against the
+//    kernel time; 2.4 GHz is the peak), the chip's power limit under this
+//    load.  The 128 x 64 tile's come to 109% (a little overlap at four waves
+//    per SIMD) with 7% more VALU instructions.
+//  * Two tile shapes share the fold.  The wide one (256 tokens x 160 rows, one
+//    workgroup per CU, below q8_0_gemm_kernel) is taken where it fills the CUs
+//    in whole rounds (m = 512, N = 20480 on MI355X); the 128 x 64 one
+//    everywhere else.  Both give bitwise the same y.
+//  * The 128 x 64 tile.  Workgroup: 8 waves over a 128-token x 64-row output
+//    tile (4 x 2 wave tiles of 32x32), two workgroups per CU (four waves per
+//    SIMD, at most 128 VGPRs each).  Each workgroup runs the whole k loop in 128-k stages; the
 //    two workgroups of a CU wait at their own barriers, out of step, so one
 //    keeps the SIMDs busy while the other waits.
 //  * LDS holds two stages per workgroup (the one computed and the one being
@@ -319,6 +328,250 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 
     }
 }
 
+// Wide tile: each wave owns 32 tokens and five 32-row weight tiles.
+//
+//  * Workgroup: 8 waves, one workgroup per CU (two waves per SIMD, up to 256
+//    VGPRs each), over 256 tokens x 160 weight rows.  At m = 512, N = 20480
+//    that is 256 workgroups, one round on the 256 CUs.
+//  * A wave's activations go straight from global memory into its MFMA operand
+//    registers (16 bytes of one block per lane); nothing else reads them, so
+//    they skip LDS.  The pair of blocks 2p, 2p + 1 is reloaded with the next
+//    stage's as soon as the stage is done with it, so one register set covers
+//    a stage and each load has a stage to land.
+//  * The 160 weight rows are shared by the 8 waves through LDS, in stages of
+//    256 k (8 blocks).  They are loaded in chunks of 4 blocks, each half-block
+//    read from its 2-byte-aligned place with one unaligned 16-byte load (the
+//    driver runs gfx9 in unaligned access mode) and its scale with a 2-byte
+//    load, then stored without realignment.
+//  * Three LDS buffers (47.6 KB each).  A stage's second chunk store is
+//    followed by the stage's one barrier, mid-stage.  After it, the next stage
+//    is complete in LDS, so its first operands are read before this stage
+//    ends.  The store into the third buffer at the start of a stage only needs
+//    every wave past the previous stage's barrier, which means done with the
+//    stage before it.
+//  * Per wave and stage, 40 tile-blocks against 12 vector-memory loads, 2-3
+//    LDS writes and 20 LDS operand reads.  The loop's VALU work is the fold
+//    plus about 2%.  Fetch is 1.20x the algorithmic reads at N = 20480,
+//    against 1.89x for the 128 x 64 tile: the two token halves of a weight
+//    tile run together on one XCD, and the activations stay in its L2.
+//  * The same fold order per output as the 128 x 64 kernel, so the two give
+//    bitwise the same y.
+constexpr int kWideWaves = 8;
+constexpr int kWideThreads = 64 * kWideWaves;
+constexpr int kWideBM = 32 * kWideWaves;   // 256 tokens per workgroup: 32 per wave
+constexpr int kWideR = 5;                  // 32-row weight tiles per wave
+constexpr int kWideBN = 32 * kWideR;       // 160 weight rows per workgroup
+constexpr int kWideSB = 8;                 // blocks per stage
+constexpr int kWideSK = kQK * kWideSB;     // 256 k per stage
+constexpr int kWideStride = kWideSK + 16;  // 272: padded LDS row of quants
+constexpr int kWideNC = kWideSB / 4;       // weight chunks (4 blocks) per stage
+constexpr int kWideNW = (2 * 4 * kWideBN + kWideThreads - 1) / kWideThreads;   // half-block slots per thread and chunk
+constexpr int kWideRS = kWideThreads / 8;  // rows between a thread's slots
+
+// One 256-k stage of the weight tile in LDS: per row the first 16 bytes of
+// blocks 0..7, then their second 16 bytes; the scale rows padded by 4 floats.
+struct WideStage {
+    uint8_t w[kWideBN * kWideStride];
+    float dw[kWideSB][kWideBN + 4];
+};
+static_assert(3 * sizeof(WideStage) <= 160 * 1024, "LDS");
+
+template <bool F8ACC>
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void q8_0_gemm_wide_kernel(
+    const uint8_t *__restrict__ w, int64_t w_row_bytes, const int8_t *__restrict__ xq, const float *__restrict__ xds,
+    float *__restrict__ y, int m, int k, int n) {
+    __shared__ __attribute__((aligned(16))) WideStage st[3];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    // the same XCD-aware order as the 128 x 64 kernel: the token tiles of a
+    // weight tile run together on one XCD
+    const int nm = (m + kWideBM - 1) / kWideBM;
+    const int ntiles = gridDim.x;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = ntiles >> 3, extra = ntiles & 7;
+    const int tile = xcd * per + min(xcd, extra) + slot;
+    const int n0 = (tile / nm) * kWideBN;
+    const int m0 = (tile - (tile / nm) * nm) * kWideBM;
+    const int nb = k / kQK;
+    const int nit = k / kWideSK;
+
+    // Resources covering the valid rows only; out-of-range loads return zeros.
+    const __amdgpu_buffer_rsrc_t rX = mmq_rsrc(xq + (int64_t)m0 * k, (int64_t)(m - m0) * k);
+    const __amdgpu_buffer_rsrc_t rD = mmq_rsrc(xds + (int64_t)m0 * nb * 2, (int64_t)(m - m0) * nb * 8);
+    const __amdgpu_buffer_rsrc_t rW = mmq_rsrc(w + (int64_t)n0 * w_row_bytes, (int64_t)(n - n0) * w_row_bytes);
+
+    const int t = lane & 31, khalf = lane >> 5;
+    // this lane's token row and k half: the A operand of block b at aoff + 32 b;
+    // the d of block 2p + khalf at doff + 16 p
+    const uint32_t aoff = (uint32_t)((32 * wave + t) * k + 16 * khalf);
+    const uint32_t doff = (uint32_t)(((32 * wave + t) * nb + khalf) * 8);
+
+    // Weight slots of a chunk: half-block q = tid + 512 j of the 160 x 4-block
+    // chunk, i.e. row (tid >> 3) + 64 j, block (tid >> 1) & 3, half tid & 1.
+    const int row0 = tid >> 3, bb0 = (tid >> 1) & 3, hh0 = tid & 1;
+    const uint32_t woq = (uint32_t)(row0 * w_row_bytes + kQ80Bytes * bb0 + 2 + 16 * hh0);   // 2-byte aligned
+    const uint32_t wod = (uint32_t)(row0 * w_row_bytes + kQ80Bytes * bb0);
+    const uint32_t wlds = (uint32_t)(row0 * kWideStride + 16 * kWideSB * hh0 + 16 * bb0);
+    const int wdw = bb0 * (kWideBN + 4) + row0;
+    struct WRegs {
+        u32x4 q[kWideNW];
+        uint32_t d[kWideNW];
+    };
+    // chunk c (blocks 4c .. 4c + 3) of stage it
+    auto load_w = [&](WRegs &Wr, int it, int c) {
+        const int sw = it * kWideSB * kQ80Bytes + c * 4 * kQ80Bytes;
+#pragma unroll
+        for (int j = 0; j < kWideNW; j++) {
+            // slots past the 1280 of a chunk (waves 4..7, last slot) read
+            // nothing: an offset beyond any range
+            const bool live = kWideThreads * (j + 1) <= 8 * kWideBN || tid + kWideThreads * j < 8 * kWideBN;
+            const uint32_t dead = live ? 0u : 0x80000000u;
+            // the row step stays in the per-lane offset, which the range check covers
+            const uint32_t ro = (uint32_t)(kWideRS * j) * (uint32_t)w_row_bytes;
+            Wr.q[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, (woq + ro) | dead, sw, 0));
+            Wr.d[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rW, (wod + ro) | dead, sw, 0);
+        }
+    };
+    auto store_w = [&](WideStage &S, const WRegs &Wr, int c) {
+#pragma unroll
+        for (int j = 0; j < kWideNW; j++) {
+            if (tid + kWideThreads * j < 8 * kWideBN) {
+                *reinterpret_cast<u32x4 *>(S.w + wlds + kWideRS * kWideStride * j + 64 * c) = Wr.q[j];
+                if (hh0 == 0) (&S.dw[0][0])[wdw + kWideRS * j + 4 * c * (kWideBN + 4)] = half_bits_to_float(Wr.d[j]);
+            }
+        }
+    };
+
+    v4i A[kWideSB];
+    float D[kWideSB / 2];
+    auto load_a = [&](int p, int it) {
+#pragma unroll
+        for (int b = 2 * p; b < 2 * p + 2; b++)
+            A[b] = __builtin_bit_cast(v4i,
+                                      __builtin_amdgcn_raw_buffer_load_b128(rX, aoff + 32 * b, it * kWideSK, 0));
+        D[p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rD, doff + 16 * p, it * kWideSB * 8, 0));
+    };
+
+    v16f acc[kWideR];
+#pragma unroll
+    for (int j = 0; j < kWideR; j++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[j][v] = 0.0f;
+
+    using BlockSum = typename std::conditional<F8ACC, v16f, v16i>::type;
+    auto block_sum = [&](const v4i &a, const v4i &b) -> BlockSum {
+        if constexpr (F8ACC) {
+            typedef long v2l __attribute__((ext_vector_type(2)));
+            const v16f zf = {0};
+            const v2l av = __builtin_bit_cast(v2l, a), bv = __builtin_bit_cast(v2l, b);
+            const v16f lo = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av[0], bv[0], zf, 0, 0, 0);
+            return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av[1], bv[1], lo, 0, 0, 0);
+        } else {
+            const v16i z = {0};
+            return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
+        }
+    };
+    // the scale products of two blocks in the block sums' layout, as in the
+    // 128 x 64 kernel
+    auto scale2 = [&](float sa, float sb) -> v32f {
+        const v32f z32 = {0};
+        return __builtin_amdgcn_mfma_f32_32x32x1f32(sa, sb, z32, 0, 0, 0);
+    };
+    auto fold = [&](v16f &ac, const BlockSum &Sb, const v32f &P, int e) {
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            if constexpr (F8ACC)
+                ac[v] = __builtin_fmaf(Sb[v], P[16 * e + v], ac[v]);
+            else
+                ac[v] = __builtin_fmaf((float)Sb[v], P[16 * e + v], ac[v]);
+        }
+    };
+    // B operands (weight rows 32 j + lane % 32) of blocks 2p, 2p + 1 and the
+    // weight scale of block 2p + khalf
+    struct BOps {
+        v4i b0, b1;
+        float sb;
+    };
+    auto rdb = [&](const WideStage &S, int p, int j) -> BOps {
+        BOps o;
+        const int brow = 32 * j + t;
+        o.b0 = *reinterpret_cast<const v4i *>(S.w + brow * kWideStride + 16 * kWideSB * khalf + 16 * (2 * p));
+        o.b1 = *reinterpret_cast<const v4i *>(S.w + brow * kWideStride + 16 * kWideSB * khalf + 16 * (2 * p + 1));
+        o.sb = S.dw[2 * p + khalf][brow];
+        return o;
+    };
+
+    // Prologue: stage 0 into st[0], its activations into the registers, and
+    // the first chunk of stage 1 into the weight registers.
+    WRegs Wr;
+    const int last = nit - 1;
+#pragma unroll
+    for (int c = 0; c < kWideNC; c++) {
+        load_w(Wr, 0, c);
+        store_w(st[0], Wr, c);
+    }
+#pragma unroll
+    for (int p = 0; p < kWideSB / 2; p++) load_a(p, 0);
+    load_w(Wr, min(1, last), 0);
+    __syncthreads();
+
+    // One stage: compute st[cur]; chunk c of stage it + 1 goes from the
+    // registers into st[nxt] at pair 2c, and the next chunk's loads are issued
+    // in its place (past the end they repeat the last stage, so the compiler's
+    // count of loads in flight stays exact).
+    BOps o = rdb(st[0], 0, 0);
+    auto stage = [&](int it, int cur, int nxt) {
+        const WideStage &S = st[cur];
+#pragma unroll
+        for (int p = 0; p < kWideSB / 2; p++) {
+#pragma unroll
+            for (int j = 0; j < kWideR; j++) {
+                const BOps c = o;
+                if (j + 1 < kWideR) o = rdb(S, p, j + 1);
+                else if (p + 1 < kWideSB / 2) o = rdb(S, p + 1, 0);
+                else o = rdb(st[nxt], 0, 0);   // complete since this stage's barrier
+                const v32f P = scale2(D[p], c.sb);
+                const BlockSum S0 = block_sum(A[2 * p], c.b0);
+                const BlockSum S1 = block_sum(A[2 * p + 1], c.b1);
+                fold(acc[j], S0, P, 0);
+                fold(acc[j], S1, P, 1);
+                asm volatile("" : "+v"(acc[j]) :: "memory");
+                if (j == kWideR - 1) load_a(p, min(it + 1, last));
+                if (j == 0 && (p & 1) == 0) {
+                    const int ch = p / 2;
+                    store_w(st[nxt], Wr, ch);
+                    if (ch + 1 < kWideNC) load_w(Wr, min(it + 1, last), ch + 1);
+                    else load_w(Wr, min(it + 2, last), 0);
+                    if (ch + 1 == kWideNC) __syncthreads();
+                }
+            }
+        }
+    };
+    int cur = 0, nxt = 1;
+#pragma unroll 1
+    for (int it = 0; it < nit; it++) {
+        stage(it, cur, nxt);
+        cur = nxt;
+        nxt = nxt == 2 ? 0 : nxt + 1;
+    }
+
+    // Output element (row 8*(v/4) + 4*khalf + v%4, column lane%32) of each
+    // wave tile: token row, weight-row column.
+#pragma unroll
+    for (int j = 0; j < kWideR; j++) {
+        const int col = n0 + 32 * j + t;
+        if (col < n) {
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int row = m0 + 32 * wave + 8 * (v >> 2) + 4 * khalf + (v & 3);
+                if (row < m) y[(int64_t)row * n + col] = acc[j][v];
+            }
+        }
+    }
+}
+
 template <bool F8ACC>
 static int launch_mmq(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, float *y, int m,
                       int k, int n, void *stream) {
@@ -327,12 +580,28 @@ static int launch_mmq(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, c
     if (k % 256 != 0) return BQM_EUNSUPPORTED;
     if (w_row_bytes < (int64_t)(k / kQK) * kQ80Bytes || w_row_bytes % 16 != 0) return BQM_EUNSUPPORTED;
     if (!aligned(w, 16) || !aligned(xq, 16) || !aligned(xds, 8) || !aligned(y, 4)) return BQM_EUNSUPPORTED;
-    // per-workgroup offsets are 32-bit: 128 rows of activations, 64 of weights
-    if ((int64_t)kMmqBM * k > 0x7FFFFFF0ll || (int64_t)kMmqBN * w_row_bytes > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
+    // per-workgroup offsets are 32-bit: up to 256 rows of activations and 160
+    // of weights (an offset with bit 31 set marks a load that reads nothing)
+    if ((int64_t)kWideBM * k > 0x7FFFFFF0ll || (int64_t)kWideBN * w_row_bytes > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
     const int64_t tiles = (int64_t)((n + kMmqBN - 1) / kMmqBN) * ((m + kMmqBM - 1) / kMmqBM);
+    const int64_t wide = (int64_t)((n + kWideBN - 1) / kWideBN) * ((m + kWideBM - 1) / kWideBM);
     if (tiles > 0x7FFFFFFF) return BQM_EUNSUPPORTED;
-    hipLaunchKernelGGL((q8_0_gemm_kernel<F8ACC>), dim3((unsigned)tiles), dim3(kMmqThreads), 0, as_stream(stream), w,
-                       w_row_bytes, xq, xds, y, m, k, n);
+    // Tile choice, counted in 32 x 32 tiles per SIMD: a wide workgroup gives
+    // each SIMD of its CU 10 tiles, one workgroup per CU per round; the
+    // 128 x 64 kernel runs two workgroups per CU, 4 tiles per SIMD per round.
+    // The wide tile does about 5% less work per tile, but only in whole rounds
+    // (a partial last round leaves CUs idle for a whole wide workgroup), so it
+    // is taken only where its rounds cost less.
+    const int64_t cus = device_cus();
+    const int64_t cost_wide = (wide + cus - 1) / cus * 95;   // 10 tiles x 0.95, in tenths
+    const int64_t cost_tall = tiles * 40 / (2 * cus);         // 4 tiles per SIMD-round, fractional rounds
+    if (cost_wide < cost_tall) {
+        hipLaunchKernelGGL((q8_0_gemm_wide_kernel<F8ACC>), dim3((unsigned)wide), dim3(kWideThreads), 0,
+                           as_stream(stream), w, w_row_bytes, xq, xds, y, m, k, n);
+    } else {
+        hipLaunchKernelGGL((q8_0_gemm_kernel<F8ACC>), dim3((unsigned)tiles), dim3(kMmqThreads), 0,
+                           as_stream(stream), w, w_row_bytes, xq, xds, y, m, k, n);
+    }
     return launch_status();
 }
 

@@ -297,6 +297,31 @@ def test_gemm_iteration_counts(bqm, k):
     assert_fold_close(y.cpu().numpy(), y_ref, T, f"gemm iterations k={k}")
 
 
+# The 256-token x 160-row MMQ tile (one workgroup per CU) is the one the
+# library takes where it fills the 256 CUs of an MI355X in whole rounds, as at
+# m=512 (or 500), N around 20480.  Its stage is 256 k and its three LDS
+# buffers rotate, so K=256, 768 and 1280 run 1, 3 and 5 stages.
+@pytest.mark.parametrize("k", [256, 768, 1280])
+def test_gemm_wide_tile_stage_counts(bqm, k):
+    rng = np.random.default_rng(100 + k)
+    m, n = 512, 20480
+    w = workloads.q8_0_weights(n, k, rng)
+    x = workloads.activations(m, k, rng, outliers=True)
+    xq, xds, xq_ref, xds_ref = quantize_both(bqm, x)
+    y = nan_like_out(m, n)
+    bqm.bqm_q8_0_gemm(dev(w), xq, xds, y)
+    torch.cuda.synchronize()
+    y_ref, T = oracle.q8_0_matmul(w, xq_ref, xds_ref, k)
+    assert_fold_close(y.cpu().numpy(), y_ref, T, f"gemm wide tile k={k}")
+
+
+def test_gemm_wide_tile_ragged_padded(bqm):
+    # m=500: the second token half holds 244 of 256 tokens; n=20400: the last
+    # of 128 row blocks holds 80 of 160 rows; rows padded by 32 bytes
+    y, y_ref, T = q8_0_case(bqm, bqm.bqm_q8_0_gemm, 500, 1280, 20400, seed=77, pad=32, outliers=True)
+    assert_fold_close(y, y_ref, T, "gemm wide tile, ragged m and n, padded rows")
+
+
 # --------------------------------------------------------------------------- e4m3
 
 
