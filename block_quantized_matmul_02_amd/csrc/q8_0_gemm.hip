@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: kept in a scalar register
     const int wm = wave >> 1, wn = wave & 1;
     // XCD-aware tile order.  Workgroups are handed to the 8 XCDs round-robin
     // (id % 8), and each XCD has its own L2.  Renumber so that XCD x runs a
@@ -318,11 +318,13 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 
 
     // Output element (row 8*(v/4) + 4*khalf + v%4, column lane%32) of the
     // wave tile.
-    const int col = n0 + wn * 32 + (lane & 31);
+    // The lane is read again (mbcnt) rather than kept live across the loop.
+    const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int col = n0 + wn * 32 + (elane & 31);
     if (col < n) {
 #pragma unroll
         for (int v = 0; v < 16; v++) {
-            const int row = m0 + wm * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
+            const int row = m0 + wm * 32 + 8 * (v >> 2) + 4 * (elane >> 5) + (v & 3);
             if (row < m) y[(int64_t)row * n + col] = acc[v];
         }
     }
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2,
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: kept in a scalar register
     // the same XCD-aware order as the 128 x 64 kernel: the token tiles of a
     // weight tile run together on one XCD
     const int nm = (m + kWideBM - 1) / kWideBM;
@@ -559,13 +561,15 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2,
 
     // Output element (row 8*(v/4) + 4*khalf + v%4, column lane%32) of each
     // wave tile: token row, weight-row column.
+    // The lane is read again (mbcnt) rather than kept live across the loop.
+    const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
     for (int j = 0; j < kWideR; j++) {
-        const int col = n0 + 32 * j + t;
+        const int col = n0 + 32 * j + (elane & 31);
         if (col < n) {
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const int row = m0 + 32 * wave + 8 * (v >> 2) + 4 * khalf + (v & 3);
+                const int row = m0 + 32 * wave + 8 * (v >> 2) + 4 * (elane >> 5) + (v & 3);
                 if (row < m) y[(int64_t)row * n + col] = acc[j][v];
             }
         }
