@@ -107,8 +107,8 @@ constexpr int kXregMaxM = 2;
 // XR: every row gives a lane the same pairs (whole rows, one pair per lane:
 // K <= 4096), so the lane's activation operands for all M tokens are loaded
 // from LDS once and held in registers.
-template <int M, bool SINGLE, int PRE, bool QX, bool XR>
-__global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
+template <int M, bool SINGLE, int PRE, bool QX, bool XR, int WG>
+__global__ __launch_bounds__(WG) void q8_0_gemv_kernel(
     const uint8_t *__restrict__ w, int64_t w_row_bytes, const int8_t *__restrict__ xq,
     const float *__restrict__ xds, const float *__restrict__ x, float *__restrict__ y, int k, int n, GemvGeom g) {
     static_assert(!QX || PRE > 0, "f32 activations are held in registers");
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
 #pragma unroll
         for (int i = 0; i < PRE; i++)
             pre_q[i] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rxq, (uint32_t)(threadIdx.x + kGemvThreads * i) * 16u, 0, 0));
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rxq, (uint32_t)(threadIdx.x + WG * i) * 16u, 0, 0));
         if (!QX) pre_d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rxd, threadIdx.x * 8u, 0, 0));
     };
     // QX: float4 number c of x (values 4c..4c+3) quantized by its 8-lane
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         if (QX) {
 #pragma unroll
             for (int i = 0; i < PRE; i++) {
-                quantize_store(as_float4(pre_q[i]), (int)threadIdx.x + kGemvThreads * i);
+                quantize_store(as_float4(pre_q[i]), (int)threadIdx.x + WG * i);
             }
             __syncthreads();
             return;
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
         const int chunks = M * k / 16;
 #pragma unroll
         for (int i = 0; i < PRE; i++) {
-            const int c = threadIdx.x + kGemvThreads * i;
+            const int c = threadIdx.x + WG * i;
             const int t = c / (k / 16);
             const int cc = c - t * (k / 16);
             const int p = cc >> 2, ci = cc & 3;
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
     };
     auto stage_activations = [&]() {
         const int chunks = M * k / 16;
-        for (int c = threadIdx.x; c < chunks; c += kGemvThreads) {
+        for (int c = threadIdx.x; c < chunks; c += WG) {
             int t = c / (k / 16);
             int cc = c - t * (k / 16);
             int p = cc >> 2, ci = cc & 3;
@@ -197,12 +197,12 @@ __global__ __launch_bounds__(kGemvThreads) void q8_0_gemv_kernel(
             int dst = t * k + 64 * p + 16 * ((ci + (p >> 2)) & 3);
             *reinterpret_cast<u32x4 *>(act_q + dst) = v;
         }
-        for (int c = threadIdx.x; c < M * nb; c += kGemvThreads) act_d[c] = xds[2 * c];
+        for (int c = threadIdx.x; c < M * nb; c += WG) act_d[c] = xds[2 * c];
         __syncthreads();
     };
 
-    const int nwaves = gridDim.x * kGemvWaves;
-    const int wid = blockIdx.x * kGemvWaves + wave;
+    const int nwaves = gridDim.x * (WG / 64);
+    const int wid = blockIdx.x * (WG / 64) + wave;
     // Waves without a tile still take part in the workgroup barrier.
     const int my_tiles = wid < g.n_row_tiles ? (g.n_row_tiles - 1 - wid) / nwaves + 1 : 0;
     const int Q = my_tiles * g.nseg;   // work items of this wave: (row tile, segment)
@@ -474,34 +474,34 @@ static bool make_geom(int k, int n, int64_t w_row_bytes, GemvGeom &g) {
     return true;
 }
 
-template <int M, bool SINGLE, int PRE, bool QX, bool XR>
+template <int M, bool SINGLE, int PRE, bool QX, bool XR, int WG>
 static int launch_variant(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
                           float *y, int k, int n, const GemvGeom &g, int grid, int lds_bytes, hipStream_t stream) {
     static LaunchCache cache;
-    const int rc = raise_lds_limit(cache, reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, SINGLE, PRE, QX, XR>),
+    const int rc = raise_lds_limit(cache, reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, SINGLE, PRE, QX, XR, WG>),
                                    160 * 1024);
     if (rc != BQM_OK) return rc;
-    hipLaunchKernelGGL((q8_0_gemv_kernel<M, SINGLE, PRE, QX, XR>), dim3(grid), dim3(kGemvThreads), lds_bytes, stream, w,
+    hipLaunchKernelGGL((q8_0_gemv_kernel<M, SINGLE, PRE, QX, XR, WG>), dim3(grid), dim3(WG), lds_bytes, stream, w,
                        w_row_bytes, xq, xds, x, y, k, n, g);
     return launch_status();
 }
 
 // Resident workgroups per CU of the pipelined variant (registers and LDS),
 // at most 4.
-template <int M, int PRE, bool QX, bool XR>
+template <int M, int PRE, bool QX, bool XR, int WG>
 static int gemv_per_cu(int lds_bytes) {
     static LaunchCache cache;
-    const void *fn = reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE, QX, XR>);
+    const void *fn = reinterpret_cast<const void *>(&q8_0_gemv_kernel<M, false, PRE, QX, XR, WG>);
     if (raise_lds_limit(cache, fn, 160 * 1024) != BQM_OK) return 1;   // allow up to 160 KiB before asking
-    return blocks_per_cu(cache, fn, kGemvThreads, lds_bytes, 4);
+    return blocks_per_cu(cache, fn, WG, lds_bytes, 4);
 }
 
 // Grid size and the pipelined / single-item choice, then the launch.
-template <int M, int PRE, bool QX, bool XR>
+template <int M, int PRE, bool QX, bool XR, int WG>
 static int launch_sized(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
                         float *y, int k, int n, const GemvGeom &g, int lds_bytes, hipStream_t stream) {
     const int cus = device_cus();
-    int per_cu = gemv_per_cu<M, PRE, QX, XR>(lds_bytes);
+    int per_cu = gemv_per_cu<M, PRE, QX, XR, WG>(lds_bytes);
     if (QX) {
         // Every workgroup of the one-launch step reads and quantizes the whole
         // f32 activation (16 KiB at K=4096), so at four workgroups per CU a
@@ -514,29 +514,29 @@ static int launch_sized(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq,
         const int cap = wbytes < (48ll << 20) ? 1 : wbytes < (128ll << 20) ? 2 : 4;
         if (per_cu > cap) per_cu = cap;
     }
-    int want = (g.n_row_tiles + kGemvWaves - 1) / kGemvWaves;
+    int want = (g.n_row_tiles + (WG / 64) - 1) / (WG / 64);
     int grid = cus * per_cu;
     if (want < grid) grid = want;
     // as few workgroups as give every wave the same number of items (the
     // last items of the longest waves otherwise run alone; measured 0.5 us
     // on the 4096 -> 64448 head)
-    const int64_t tpw = ((int64_t)g.n_row_tiles + (int64_t)grid * kGemvWaves - 1) / ((int64_t)grid * kGemvWaves);
-    grid = (int)(((int64_t)g.n_row_tiles + tpw * kGemvWaves - 1) / (tpw * kGemvWaves));
+    const int64_t tpw = ((int64_t)g.n_row_tiles + (int64_t)grid * (WG / 64) - 1) / ((int64_t)grid * (WG / 64));
+    grid = (int)(((int64_t)g.n_row_tiles + tpw * (WG / 64) - 1) / (tpw * (WG / 64)));
     // every wave holds at most one item: the variant without the pipeline
-    const bool single = (int64_t)g.n_row_tiles * g.nseg <= (int64_t)grid * kGemvWaves;
+    const bool single = (int64_t)g.n_row_tiles * g.nseg <= (int64_t)grid * (WG / 64);
     if (single)
-        return launch_variant<M, true, PRE, QX, XR>(w, w_row_bytes, xq, xds, x, y, k, n, g, grid, lds_bytes, stream);
-    return launch_variant<M, false, PRE, QX, XR>(w, w_row_bytes, xq, xds, x, y, k, n, g, grid, lds_bytes, stream);
+        return launch_variant<M, true, PRE, QX, XR, WG>(w, w_row_bytes, xq, xds, x, y, k, n, g, grid, lds_bytes, stream);
+    return launch_variant<M, false, PRE, QX, XR, WG>(w, w_row_bytes, xq, xds, x, y, k, n, g, grid, lds_bytes, stream);
 }
 
-template <int M, int PRE, bool QX>
+template <int M, int PRE, bool QX, int WG = kGemvThreads>
 static int launch_xr(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, const float *xds, const float *x,
                      float *y, int k, int n, const GemvGeom &g, int lds_bytes, hipStream_t stream) {
     if constexpr (M <= kXregMaxM) {
         if (g.nseg == 1 && g.J == 1)
-            return launch_sized<M, PRE, QX, true>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+            return launch_sized<M, PRE, QX, true, WG>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
     }
-    return launch_sized<M, PRE, QX, false>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
+    return launch_sized<M, PRE, QX, false, WG>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds_bytes, stream);
 }
 
 template <int M>
@@ -546,6 +546,22 @@ static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, 
     const int act_bytes = (M * k + M * nb * 4 + 15) & ~15;
     const int lds_bytes = act_bytes + kGemvWaves * 2 * g.TB;
     if constexpr (M <= 2) {
+        if (x && (int64_t)n * w_row_bytes < (48ll << 20) && g.RT == 1 && n >= 16 * device_cus()) {
+            // The one-launch step runs one workgroup per CU below 48 MB of
+            // weights (below).  With one row per tile and at least 16 rows per
+            // CU, that workgroup has 16 waves, so all of a CU's rows are in
+            // flight at once while the activation is still quantized once per
+            // CU (measured in a graph, bitwise the same: m=1 4096->4096 6.77 ->
+            // 6.58 us, 4096->5152 7.68 -> 7.49, m=2 4096->4096 8.68 -> 7.40;
+            // at K=1280, two rows per tile, it was slower: 3.84 -> 4.71).
+            constexpr int WG = 1024;
+            const int lds16 = act_bytes + (WG / 64) * 2 * g.TB;
+            const int f4 = (M * k / 4 + WG - 1) / WG;
+            if (lds16 <= 160 * 1024) {
+                if (f4 <= 1) return launch_xr<M, 1, true, WG>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds16, stream);
+                return launch_xr<M, 2, true, WG>(w, w_row_bytes, xq, xds, x, y, k, n, g, lds16, stream);
+            }
+        }
         if (x) {
             // f32 activations held in registers, 1, 2, 4 or 8 float4s per
             // thread (the entry point admits m <= 2, m*k <= 8192)

@@ -59,7 +59,10 @@ def both_paths(bqm, w, x):
 
 
 CASES = [(1, 256, 1), (1, 256, 47), (2, 512, 100), (1, 1280, 67), (1, 2048, 300), (1, 4096, 4096),
-         (2, 4096, 129), (1, 8192, 65), (2, 1280, 4096), (1, 4096, 5152), (2, 2048, 77)]
+         (2, 4096, 129), (1, 8192, 65), (2, 1280, 4096), (1, 4096, 5152), (2, 2048, 77),
+         # 16-wave workgroups of the one-launch step (one row per tile, at least
+         # 16 rows per CU): one item per wave, and two with a ragged last one
+         (2, 4096, 4096), (1, 3072, 4100)]
 
 
 @pytest.mark.parametrize("m,k,n", CASES)
