@@ -363,7 +363,7 @@ def main():
             "config": {"workload": "decode head GEMV: m=1, K=4096, N=64448, Q8_0 weights, f32 activation "
                                    "quantized on the device to q8_1 (in the GEMV launch)",
                        "m": m, "k": k, "n": n, "weight_copies_rotated": ROTATE, "parallelism": "none"},
-            "roofline": {"bound": "hbm", "kernel": "q8_0_gemv_kernel<1, false, 4, true, true, 256>",
+            "roofline": {"bound": "hbm", "kernel": "q8_0_gemv_kernel<1, false, 1, true, true, 1024>",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                          "bytes_per_launch": step_bytes, "avg_launch_us": round(per["gemv_f32"] * 1e3, 3)},

@@ -546,14 +546,18 @@ static int launch_gemv(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, 
     const int act_bytes = (M * k + M * nb * 4 + 15) & ~15;
     const int lds_bytes = act_bytes + kGemvWaves * 2 * g.TB;
     if constexpr (M <= 2) {
-        if (x && (int64_t)n * w_row_bytes < (48ll << 20) && g.RT == 1 && n >= 16 * device_cus()) {
-            // The one-launch step runs one workgroup per CU below 48 MB of
-            // weights (below).  With one row per tile and at least 16 rows per
-            // CU, that workgroup has 16 waves, so all of a CU's rows are in
-            // flight at once while the activation is still quantized once per
-            // CU (measured in a graph, bitwise the same: m=1 4096->4096 6.77 ->
+        const int64_t wbytes16 = (int64_t)n * w_row_bytes;
+        if (x && (wbytes16 < (48ll << 20) || wbytes16 >= (128ll << 20)) && g.RT == 1 && n >= 16 * device_cus()) {
+            // One 16-wave workgroup per CU for the one-launch step, where a
+            // tile is one row and every CU gets at least 16 rows: all of a
+            // CU's rows are in flight at once while the activation is
+            // quantized once per CU instead of once per 4-wave workgroup.
+            // Measured in a graph, bitwise the same: m=1 4096->4096 6.77 ->
             // 6.58 us, 4096->5152 7.68 -> 7.49, m=2 4096->4096 8.68 -> 7.40;
-            // at K=1280, two rows per tile, it was slower: 3.84 -> 4.71).
+            // the 4096->64448 head m=1 44.25 -> 43.79 and 44.17 -> 43.95, m=2
+            // 47.31 -> 45.27.  Not taken between 48 and 128 MB (4096->20480:
+            // 15.93 -> 16.34, where 4-wave workgroups run two per CU) nor at
+            // K=1280, two rows per tile (3.84 -> 4.71).
             constexpr int WG = 1024;
             const int lds16 = act_bytes + (WG / 64) * 2 * g.TB;
             const int f4 = (M * k / 4 + WG - 1) / WG;

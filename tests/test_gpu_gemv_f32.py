@@ -111,15 +111,16 @@ def test_gemv_f32_refuses_beyond_decode(bqm, m, k):
         bqm.bqm_q8_0_gemv_f32(w, x)
 
 
-def test_gemv_f32_decode_head(bqm):
-    # the decode head, K=4096 -> N=64448 at m=1: bitwise against the two-call
-    # path and against the oracle on every output
-    m, k, n = 1, 4096, 64448
-    rng = np.random.default_rng(0)
+@pytest.mark.parametrize("m", [1, 2])
+def test_gemv_f32_decode_head(bqm, m):
+    # the decode head, K=4096 -> N=64448 at m=1 and 2: bitwise against the
+    # two-call path and against the oracle on every output
+    k, n = 4096, 64448
+    rng = np.random.default_rng(m)
     w = workloads.q8_0_weights(n, k, rng)
     x = workloads.activations(m, k, rng)
     y1, y2 = both_paths(bqm, w, x)
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
     xq_ref, xds_ref = oracle.q8_1_quantize(x)
     y_ref, T = oracle.q8_0_matmul(w, xq_ref, xds_ref, k)
-    close(y1, y_ref, T, "gemv_f32 head")
+    close(y1, y_ref, T, f"gemv_f32 head m={m}")
