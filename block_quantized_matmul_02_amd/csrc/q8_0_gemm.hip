@@ -351,6 +351,10 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 
 //    ends.  The store into the third buffer at the start of a stage only needs
 //    every wave past the previous stage's barrier, which means done with the
 //    stage before it.
+//  * The loop runs three stages per trip, so the buffer indices are
+//    compile-time constants (one or two stages follow the loop), and the
+//    epilogue stores through a range-checked resource over the workgroup's
+//    rows of y, one address add per store and no branch (about 1% together).
 //  * Per wave and stage, 40 tile-blocks against 12 vector-memory loads, 2-3
 //    LDS writes and 20 LDS operand reads.  The loop's VALU work is the fold
 //    plus about 2%.  Fetch is 1.20x the algorithmic reads at N = 20480,
@@ -551,27 +555,39 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2,
             }
         }
     };
-    int cur = 0, nxt = 1;
+    // three stages per trip, so the buffer indices are compile-time
+    // constants; one or two stages after the loop
+    int it = 0;
 #pragma unroll 1
-    for (int it = 0; it < nit; it++) {
-        stage(it, cur, nxt);
-        cur = nxt;
-        nxt = nxt == 2 ? 0 : nxt + 1;
+    for (; it + 3 <= nit; it += 3) {
+        stage(it, 0, 1);
+        stage(it + 1, 1, 2);
+        stage(it + 2, 2, 0);
     }
+    if (it < nit) stage(it, 0, 1);
+    if (it + 1 < nit) stage(it + 1, 1, 2);
 
     // Output element (row 8*(v/4) + 4*khalf + v%4, column lane%32) of each
     // wave tile: token row, weight-row column.
-    // The lane is read again (mbcnt) rather than kept live across the loop.
+    // Stores through a resource over this workgroup's rows of y (m0 .. m - 1):
+    // rows past m fall outside it, and columns past n get an offset beyond any
+    // range, so no store needs a branch (the launch keeps every offset below
+    // 2^31).  The lane is read again (mbcnt) rather than kept live across the
+    // loop.
     const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const __amdgpu_buffer_rsrc_t rY = mmq_rsrc(y + (int64_t)m0 * n, (int64_t)(m - m0) * n * 4);
+    const uint32_t n4 = (uint32_t)n * 4u;
+    const uint32_t ybase = ((uint32_t)(32 * wave + 4 * (elane >> 5)) * (uint32_t)n + (uint32_t)(n0 + (elane & 31))) * 4u;
 #pragma unroll
     for (int j = 0; j < kWideR; j++) {
-        const int col = n0 + 32 * j + (elane & 31);
-        if (col < n) {
+        const uint32_t cb = n0 + 32 * j + (elane & 31) < n ? ybase + 128u * j : 0x80000000u;
 #pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const int row = m0 + 32 * wave + 8 * (v >> 2) + 4 * (elane >> 5) + (v & 3);
-                if (row < m) y[(int64_t)row * n + col] = acc[j][v];
-            }
+        for (int v = 0; v < 16; v++) {
+            const uint32_t ro = (uint32_t)(8 * (v >> 2) + (v & 3)) * n4;
+            // copied to a scalar first: a bit cast of a vector-element
+            // expression is lowered to a read of element 0
+            const float val = acc[j][v];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, val), rY, cb + ro, 0, 0);
         }
     }
 }
@@ -599,7 +615,9 @@ static int launch_mmq(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, c
     const int64_t cus = device_cus();
     const int64_t cost_wide = (wide + cus - 1) / cus * 95;   // 10 tiles x 0.95, in tenths
     const int64_t cost_tall = tiles * 40 / (2 * cus);         // 4 tiles per SIMD-round, fractional rounds
-    if (cost_wide < cost_tall) {
+    // the wide tile's output offsets ((256 + 32) rows of y, and a dead column
+    // offset of 2^31 plus 27 rows) stay in 32 bits
+    if (cost_wide < cost_tall && (int64_t)(kWideBM + 32) * n * 4 <= 0x7FFFFFF0ll) {
         hipLaunchKernelGGL((q8_0_gemm_wide_kernel<F8ACC>), dim3((unsigned)wide), dim3(kWideThreads), 0,
                            as_stream(stream), w, w_row_bytes, xq, xds, y, m, k, n);
     } else {

@@ -299,9 +299,10 @@ def test_gemm_iteration_counts(bqm, k):
 
 # The 256-token x 160-row MMQ tile (one workgroup per CU) is the one the
 # library takes where it fills the 256 CUs of an MI355X in whole rounds, as at
-# m=512 (or 500), N around 20480.  Its stage is 256 k and its three LDS
-# buffers rotate, so K=256, 768 and 1280 run 1, 3 and 5 stages.
-@pytest.mark.parametrize("k", [256, 768, 1280])
+# m=512 (or 500), N around 20480.  Its stage is 256 k, its three LDS buffers
+# rotate and the loop runs three stages per trip, so K=256, 512, 768, 1024 and
+# 1280 (1..5 stages) cover every count of whole trips and leftover stages.
+@pytest.mark.parametrize("k", [256, 512, 768, 1024, 1280])
 def test_gemm_wide_tile_stage_counts(bqm, k):
     rng = np.random.default_rng(100 + k)
     m, n = 512, 20480
