@@ -259,22 +259,28 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
             // the tile, and the scale xs[t] * g of its 16 outputs is one value
             // (one multiply and 16 fma per tile instead of 16 of each).
             const float sxt = S.xs[wm * 32 + (lane & 31)];
-            auto part = [&](int j) {
-                const v8i b0 = ld8(pb + j * 32 * kB8RowStride), b1 = ld8(pb + j * 32 * kB8RowStride + 64);
-                v16f P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0, a0, z, 0, 0, 0, 127, 0, 127);
-                return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1, a1, P, 0, 0, 0, 127, 0, 127);
+            struct BT { v8i b0, b1; };
+            auto rdt = [&](int j) -> BT { return BT{ld8(pb + j * 32 * kB8RowStride), ld8(pb + j * 32 * kB8RowStride + 64)}; };
+            auto part = [&](const BT &b) {
+                v16f P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b.b0, a0, z, 0, 0, 0, 127, 0, 127);
+                return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b.b1, a1, P, 0, 0, 0, 127, 0, 127);
             };
             // Three partial sets, indexed at compile time: tiles j+1 and j+2
-            // are on the matrix cores while tile j is folded.  A fold that
-            // reads the MFMA results issued just before it barely overlaps
-            // them (measured: 21% of the fold's time hidden, 62% two tiles
-            // behind).
+            // are on the matrix cores while tile j is folded; the operands of
+            // tile j+3 are read from LDS meanwhile.
             v16f P[3];
-            P[0] = part(0);
-            P[1] = part(1);
+            BT bn = rdt(0);
+            P[0] = part(bn);
+            bn = rdt(1);
+            P[1] = part(bn);
+            if (2 < NT) bn = rdt(2);
 #pragma unroll
             for (int j = 0; j < NT; j++) {
-                if (j + 2 < NT) P[(j + 2) % 3] = part(j + 2);
+                if (j + 2 < NT) {
+                    const BT cur = bn;
+                    if (j + 3 < NT) bn = rdt(j + 3);
+                    P[(j + 2) % 3] = part(cur);
+                }
                 const float sj = sxt * G[j];
 #pragma unroll
                 for (int v = 0; v < 16; v++) acc[j][v] = __builtin_fmaf(P[j % 3][v], sj, acc[j][v]);
