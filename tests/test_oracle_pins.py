@@ -58,7 +58,7 @@ def test_q8_1_ties_round_half_away_from_zero(page):
     expect = np.concatenate([[127], k_vals.astype(np.int64) + 1])
     assert np.array_equal(xq[0].astype(np.int64), expect)
     assert np.array_equal(xq[1].astype(np.int64), -expect)
-    # the pages' int8 quantizer emits +-127 at the block amax
+    # on the pages the int8 code of a block's largest magnitude is +-127
     assert page["int8_quantizer_amax_code"]["value"] == 127
 
 
