@@ -9,14 +9,18 @@
 // multiplier and this folded scale, in that order); the output is the
 // activation times the transposed e4m3 weight, with no host synchronization.
 //
-// Quantization is three launches on the caller's stream, with no atomics and
+// Quantization is two launches on the caller's stream, with no atomics and
 // no scratch allocation:
-//   1. partial maxima of |x|, one per workgroup, parked in the first bytes of
-//      the xq output buffer (it is overwritten in step 3 anyway);
-//   2. one workgroup reduces the partials and writes the 4-float scale block;
-//   3. every value is scaled by scales[1], clamped to +-448 and converted with
-//      the hardware round-to-nearest-even converter (v_cvt_pk_fp8_f32).
-// The result is deterministic (max is exact and order-free).
+//   1. partial maxima of |x|, one per workgroup (at most 256), each written
+//      into every quantize workgroup's region of the xq output buffer: region
+//      j is the first 256 4-byte words that quantize workgroup j writes;
+//   2. each quantize workgroup reduces the partials in its own region, so it
+//      has the batch amax, before a barrier after which it overwrites them;
+//      it scales every value of its share by 448/amax, clamps to +-448 and
+//      converts with the hardware round-to-nearest-even converter
+//      (v_cvt_pk_fp8_f32); workgroup 0 writes the 4-float scale block.
+// The result is deterministic (max is exact and order-free), and every
+// workgroup forms the same amax and multiplier.
 //
 // The GEMM uses v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales
 // (E8M0 127 = 2^0): 32x32 outputs per 64-deep step, f32 accumulation, the
@@ -32,8 +36,10 @@
 
 namespace bqm {
 
-constexpr int kAmaxThreads = 256;
-constexpr int kAmaxMaxBlocks = 2048;
+constexpr int kAmaxThreads = 1024;   // partial-max workgroup, at most (512 below 64 full workgroups)
+constexpr int kAmaxMaxBlocks = 64;   // partials; each takes one 4-byte word of every region
+constexpr int kQuantThreads = 256;   // quantize workgroup; its region is its first 256 words
+constexpr int kQuantMaxBlocks = 4096;
 
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
@@ -44,6 +50,8 @@ __device__ __forceinline__ float wave_max(float v) {
     return swap32_max(v);
 }
 
+// Max over the workgroup, returned to every thread; `red` holds one float per
+// wave.  Every thread's v is final before the barrier.
 __device__ __forceinline__ float block_max(float v, float *red) {
     v = wave_max(v);
     const int wave = threadIdx.x >> 6;
@@ -54,14 +62,16 @@ __device__ __forceinline__ float block_max(float v, float *red) {
     return r;
 }
 
-// Step 1: partial[blockIdx.x] = max |x| over a grid-strided share of x.
+// Step 1: the max |x| over a grid-strided share of x, written to word
+// 256 j + blockIdx.x of xq for every quantize workgroup j < nq (one scattered
+// 4-byte store per region and partial: few, wide workgroups keep them few).
 __global__ __launch_bounds__(kAmaxThreads) void e4m3_amax_partial_kernel(const float4 *__restrict__ x, int64_t nvec,
-                                                                         int64_t count, float *__restrict__ partial) {
+                                                                         float *__restrict__ regions, int nq) {
     __shared__ float red[kAmaxThreads / 64];
     float a = 0.0f;
     // four independent 16-byte loads in flight per thread and step
-    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-    int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (; i + 3 * stride < nvec; i += 4 * stride) {
         float4 v[4];
 #pragma unroll
@@ -74,47 +84,51 @@ __global__ __launch_bounds__(kAmaxThreads) void e4m3_amax_partial_kernel(const f
         float4 v = x[i];
         a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
-    (void)count;
-    float r = block_max(a, red);
-    if (threadIdx.x == 0) partial[blockIdx.x] = r;
+    const float r = block_max(a, red);
+    for (int j = threadIdx.x; j < nq; j += blockDim.x) regions[(int64_t)j * kQuantThreads + blockIdx.x] = r;
 }
 
-// Step 2: reduce the partials and write the scale block.
-__global__ __launch_bounds__(kAmaxThreads) void e4m3_amax_finalize_kernel(const float *__restrict__ partial, int np,
-                                                                          float w_scale, float *__restrict__ scales) {
-    __shared__ float red[kAmaxThreads / 64];
-    float a = 0.0f;
-    for (int i = threadIdx.x; i < np; i += kAmaxThreads) a = fmaxf(a, partial[i]);
-    float amax = block_max(a, red);
-    if (threadIdx.x == 0) {
-        float mul = 0.0f, xs = 0.0f;
-        if (amax > 0.0f) {
-            mul = 448.0f / amax;
-            xs = amax / 448.0f;
-        }
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// Step 2: the batch amax from this workgroup's region (np partials), then
+// xq = e4m3(clamp(x * 448/amax)), four values per thread and step.  The first
+// step's loads are issued before the region is reduced.  The region is the
+// first word of each thread's first store, read before the barrier in
+// block_max, so no store of this workgroup can land before every read.
+__global__ __launch_bounds__(kQuantThreads) void e4m3_quantize_kernel(const float4 *__restrict__ x, int64_t nvec,
+                                                                      int np, float w_scale,
+                                                                      float *__restrict__ scales,
+                                                                      unsigned *__restrict__ xq) {
+    __shared__ float red[kQuantThreads / 64];
+    const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+    const int64_t i0 = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) v[u] = i0 + u * stride < nvec ? x[i0 + u * stride] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float *region = reinterpret_cast<const float *>(xq) + (int64_t)blockIdx.x * kQuantThreads;
+    const float amax = block_max((int)threadIdx.x < np ? region[threadIdx.x] : 0.0f, red);
+    float mul = 0.0f, xs = 0.0f;
+    if (amax > 0.0f) {
+        mul = 448.0f / amax;
+        xs = amax / 448.0f;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         scales[0] = amax;
         scales[1] = mul;
         scales[2] = xs * w_scale;
         scales[3] = xs;
     }
-}
-
-__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
-
-// Step 3: xq = e4m3(clamp(x * mul)), four values per thread.
-__global__ __launch_bounds__(256) void e4m3_quantize_kernel(const float4 *__restrict__ x, int64_t nvec,
-                                                            const float *__restrict__ scales,
-                                                            unsigned *__restrict__ xq) {
-    const float mul = scales[1];
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    auto q4 = [&](float4 v) {
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v.x * mul), clamp448(v.y * mul), 0, false);
-        return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(v.z * mul), clamp448(v.w * mul), lo, true);
+    auto q4 = [&](float4 f) {
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(f.x * mul), clamp448(f.y * mul), 0, false);
+        return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(f.z * mul), clamp448(f.w * mul), lo, true);
     };
-    // four independent 16-byte loads in flight per thread and step
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+        if (i0 + u * stride < nvec) xq[i0 + u * stride] = q4(v[u]);
+    // past the first step (only where the grid is capped), four independent
+    // 16-byte loads in flight per thread and step
+    int64_t i = i0 + 4 * stride;
     for (; i + 3 * stride < nvec; i += 4 * stride) {
-        float4 v[4];
 #pragma unroll
         for (int u = 0; u < 4; u++) v[u] = x[i + u * stride];
 #pragma unroll
@@ -348,26 +362,25 @@ extern "C" int bqm_e4m3_quantize_amax(const float *x, uint8_t *xq, float *scales
     if (!aligned(x, 16) || !aligned(xq, 4) || !aligned(scales, 4)) return BQM_EUNSUPPORTED;
     const int64_t count = (int64_t)m * k;
     const int64_t nvec = count / 4;
-    // partials live in xq: nblocks floats must fit in count bytes
-    int64_t nblocks = (nvec + kAmaxThreads * 4 - 1) / (kAmaxThreads * 4);
-    if (nblocks > kAmaxMaxBlocks) nblocks = kAmaxMaxBlocks;
-    if (nblocks > count / 4) nblocks = count / 4;
-    if (nblocks < 1) nblocks = 1;
+    // quantize workgroups: one pass of four loads per thread where the grid
+    // allows; partial workgroups: at most one per word of a region
+    int64_t nq = (nvec + kQuantThreads * 4 - 1) / (kQuantThreads * 4);
+    if (nq > kQuantMaxBlocks) nq = kQuantMaxBlocks;
+    const int pt = nvec >= (int64_t)kAmaxMaxBlocks * kAmaxThreads * 4 ? kAmaxThreads : kAmaxThreads / 2;
+    int64_t np = (nvec + pt * 4 - 1) / (pt * 4);
+    if (np > kAmaxMaxBlocks) np = kAmaxMaxBlocks;
+    // region j (words 256 j .. 256 j + np - 1) lies in the words quantize
+    // workgroup j writes in its first step: words 256 j + t, t < 256, below nvec
+    if (np > nvec - (nq - 1) * kQuantThreads) np = nvec - (nq - 1) * kQuantThreads;
+    if (np < 1 || np > kQuantThreads) return BQM_EINVAL;   // unreachable for nvec >= 1
     hipStream_t s = as_stream(stream);
-    float *partial = reinterpret_cast<float *>(xq);
-    hipLaunchKernelGGL(e4m3_amax_partial_kernel, dim3((unsigned)nblocks), dim3(kAmaxThreads), 0, s,
-                       reinterpret_cast<const float4 *>(x), nvec, count, partial);
-    int rc = launch_status();
+    hipLaunchKernelGGL(e4m3_amax_partial_kernel, dim3((unsigned)np), dim3(pt), 0, s,
+                       reinterpret_cast<const float4 *>(x), nvec, reinterpret_cast<float *>(xq), (int)nq);
+    const int rc = launch_status();
     if (rc) return rc;
-    hipLaunchKernelGGL(e4m3_amax_finalize_kernel, dim3(1), dim3(kAmaxThreads), 0, s, partial, (int)nblocks, w_scale,
-                       scales);
-    rc = launch_status();
-    if (rc) return rc;
-    int64_t qblocks = (nvec + 256 * 4 - 1) / (256 * 4);
-    if (qblocks > 4096) qblocks = 4096;
-    if (qblocks < 1) qblocks = 1;
-    hipLaunchKernelGGL(e4m3_quantize_kernel, dim3((unsigned)qblocks), dim3(256), 0, s,
-                       reinterpret_cast<const float4 *>(x), nvec, scales, reinterpret_cast<unsigned *>(xq));
+    hipLaunchKernelGGL(e4m3_quantize_kernel, dim3((unsigned)nq), dim3(kQuantThreads), 0, s,
+                       reinterpret_cast<const float4 *>(x), nvec, (int)np, w_scale, scales,
+                       reinterpret_cast<unsigned *>(xq));
     return launch_status();
 }
 

@@ -152,7 +152,9 @@ int bqm_q8_0_gemm_f8acc(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq,
  *   w_scale : the weight tensor's per-tensor scale, finite (else EINVAL).
  *   m >= 1, k >= 4, k % 4 == 0 (else BQM_EUNSUPPORTED).
  * xq = e4m3(clamp(x * mul, -448, 448)), round to nearest even, sign of
- * zero kept; NaN codes (magnitude 0x7F) are never written.
+ * zero kept; NaN codes (magnitude 0x7F) are never written.  Two launches on
+ * the stream; between them xq holds the partial maxima (it is the only
+ * working memory), so it must not alias x or scales.
  */
 int bqm_e4m3_quantize_amax(const float *x, uint8_t *xq, float *scales, float w_scale, int m,
                            int k, void *stream);

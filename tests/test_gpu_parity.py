@@ -333,7 +333,14 @@ def e4m3_quantize_both(bqm, x, w_scale):
     return xq, sc, xq_ref, sc_ref
 
 
-@pytest.mark.parametrize("m,k", [(1, 4), (3, 100), (7, 1000), (64, 4096), (512, 4096)])
+# The partial maxima travel in the xq buffer: region j (the first 256 words
+# quantize workgroup j writes) holds one word per partial workgroup.  The
+# shapes cover one and two quantize workgroups with a single partial (257 x 4,
+# 5 x 1028), a partial count below the cap (1000 x 1024: 63 partials, 250
+# regions), the cap of 256 partials (512 and 2048 x 4096) and the cap of 4096
+# quantize workgroups with a grid-strided tail (4100 x 4096).
+@pytest.mark.parametrize("m,k", [(1, 4), (3, 100), (7, 1000), (257, 4), (5, 1028), (64, 4096), (1000, 1024),
+                                 (512, 4096), (2048, 4096), (4100, 4096)])
 def test_e4m3_quantize_bit_exact(bqm, m, k):
     rng = np.random.default_rng(50 + m)
     x = workloads.activations(m, k, rng, outliers=True)
