@@ -17,9 +17,9 @@
 //    on 16 lanes; no packed f32).  Counters of the full kernels at m=512,
 //    K=4096, N=20480: VALU busy is exactly 4 cycles per VALU instruction and
 //    the matrix core is busy exactly its instructions' cycles.  For the wide
-//    tile the two add up to 98% of the SQ busy cycles (per shader engine), so
+//    tile the two add up to 97-98% of the SQ busy cycles (per shader engine), so
 //    its SIMDs hardly ever wait and the fold is the bound; those launches ran
-//    at about 1.8 GHz (SQ_BUSY_CYCLES over the 32 shader engines against the
+//    at 1.8-2.1 GHz (SQ_BUSY_CYCLES over the 32 shader engines against the
 //    kernel time; 2.4 GHz is the peak), the chip's power limit under this
 //    load.  The 128 x 64 tile's come to 109% (a little overlap at four waves
 //    per SIMD) with 7% more VALU instructions.
