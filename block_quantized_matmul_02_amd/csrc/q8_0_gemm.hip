@@ -23,15 +23,20 @@
 //    kernel time; 2.4 GHz is the peak), the chip's power limit under this
 //    load.  The 128 x 64 tile's come to 109% (a little overlap at four waves
 //    per SIMD) with 7% more VALU instructions.
-//  * Two tile shapes share the fold.  The wide one (256 tokens x 160 rows, one
+//  * Three tile shapes share the fold; the launch picks one by the time of
+//    the busiest CU (launch_mmq).  The wide one (256 tokens x 160 rows, one
 //    workgroup per CU, below q8_0_gemm_kernel) is taken where it fills the CUs
-//    in whole rounds (m = 512, N = 20480 on MI355X); the 128 x 64 one
-//    everywhere else.  Both give bitwise the same y.
-//  * The 128 x 64 tile.  Workgroup: 8 waves over a 128-token x 64-row output
-//    tile (4 x 2 wave tiles of 32x32), two workgroups per CU (four waves per
-//    SIMD, at most 128 VGPRs each).  Each workgroup runs the whole k loop in 128-k stages; the
-//    two workgroups of a CU wait at their own barriers, out of step, so one
-//    keeps the SIMDs busy while the other waits.
+//    in whole rounds (m = 512, N = 20480 on MI355X); the 128 x 96 one where
+//    128 x 64 workgroups would give some CUs a second one in a round (N = 5152
+//    and 6144); the 128 x 64 one everywhere else.  All give bitwise the same y.
+//  * The 128 x 64 and 128 x 96 tiles (q8_0_gemm_kernel<F8ACC, WN>, WN = 2 or
+//    3).  Workgroup: 4 x WN waves over a 128-token x 32*WN-row output tile of
+//    32x32 wave tiles.  The 64-row tile runs two workgroups per CU (four waves
+//    per SIMD, at most 128 VGPRs each), which wait at their own barriers, out
+//    of step, so one keeps the SIMDs busy while the other waits; the 96-row
+//    tile one workgroup of 12 waves (three per SIMD, at most 170 VGPRs), so
+//    that no SIMD has more than three tiles at N = 5152.  Each workgroup runs
+//    the whole k loop in 128-k stages.
 //  * LDS holds two stages per workgroup (the one computed and the one being
 //    filled), 30 KB each.  The next stage's global loads are in registers
 //    while a stage is computed; they are stored to the other buffer during
@@ -81,10 +86,8 @@
 namespace bqm {
 
 constexpr int kMmqBM = 128;                  // tokens per workgroup tile
-constexpr int kMmqBN = 64;                   // weight rows per workgroup tile
 constexpr int kMmqSK = 128;                  // k values per stage = 4 blocks
 constexpr int kMmqSB = kMmqSK / kQK;         // 4
-constexpr int kMmqThreads = 512;             // 8 waves: 4 x 2 output waves
 constexpr int kMmqStride = kMmqSK + 16;      // 144: padded LDS row of quants
 constexpr int kMmqPairBytes = 2 * kQ80Bytes; // 68
 
@@ -98,14 +101,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mmq_rsrc(const void *base, int
 // store one half of a row write 64 consecutive bytes.  The scale rows are
 // padded by 4 floats so the stores of different blocks fall in different
 // banks.
+template <int WN>
 struct MmqStage {
     uint8_t x[kMmqBM * kMmqStride];
-    uint8_t w[kMmqBN * kMmqStride];
+    uint8_t w[32 * WN * kMmqStride];
     float dx[kMmqSB][kMmqBM + 4];
-    float dw[kMmqSB][kMmqBN + 4];
+    float dw[kMmqSB][32 * WN + 4];
 };
-// two buffers (the stage computed and the one being filled), two workgroups per CU
-static_assert(4 * sizeof(MmqStage) <= 160 * 1024, "LDS");
+// two buffers (the stage computed and the one being filled); two workgroups
+// per CU for the 64-row tile, one for the 96-row tile
+static_assert(4 * sizeof(MmqStage<2>) <= 160 * 1024 && 2 * sizeof(MmqStage<3>) <= 160 * 1024, "LDS");
 
 // Global loads of one stage (128 k), held in registers until stored to LDS:
 // two 16-byte activation chunks, one half-block of weights (16 quants, from a
@@ -117,16 +122,20 @@ struct MmqRegs {
     float dx;
 };
 
-template <bool F8ACC>
-__global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void q8_0_gemm_kernel(
-    const uint8_t *__restrict__ w, int64_t w_row_bytes, const int8_t *__restrict__ xq, const float *__restrict__ xds,
-    float *__restrict__ y, int m, int k, int n) {
-    __shared__ __attribute__((aligned(16))) MmqStage st[2];
+template <bool F8ACC, int WN>
+__global__ __launch_bounds__(256 * WN) __attribute__((amdgpu_waves_per_eu(WN == 2 ? 4 : 3, WN == 2 ? 4 : 3))) void
+q8_0_gemm_kernel(const uint8_t *__restrict__ w, int64_t w_row_bytes, const int8_t *__restrict__ xq,
+                 const float *__restrict__ xds, float *__restrict__ y, int m, int k, int n) {
+    static_assert(WN == 2 || WN == 3, "64- or 96-row tile");
+    constexpr int kMmqBN = 32 * WN;              // weight rows per workgroup tile
+    constexpr int kMmqThreads = 256 * WN;        // 4 x WN output waves
+    using MmqStageT = MmqStage<WN>;
+    __shared__ __attribute__((aligned(16))) MmqStageT st[2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: kept in a scalar register
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = (int)((unsigned)wave / WN), wn = (int)((unsigned)wave % WN);
     // XCD-aware tile order.  Workgroups are handed to the 8 XCDs round-robin
     // (id % 8), and each XCD has its own L2.  Renumber so that XCD x runs a
     // contiguous range of tiles, m-tile fastest: the token tiles that share a
@@ -148,10 +157,12 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 
 
     // Load slots, fixed for the kernel (the stage's offset is a uniform
     // scalar added by the buffer load).
-    //  X: chunk q = tid + 512*j of the 128 x 128-byte activation tile: row
-    //     q >> 3, 16-byte chunk q & 7.
-    //  dX: (row tid >> 2, block tid & 3), the d of each (d, s) pair.
-    //  W: half-block q = tid of the 64 x 4-block weight tile: row q >> 3,
+    //  X: chunk q = tid + kMmqThreads*j of the 128 x 128-byte activation
+    //     tile (q < 1024): row q >> 3, 16-byte chunk q & 7.  With 768 threads
+    //     the second slot of threads 256.. is empty: it reads nothing (an
+    //     offset beyond any range) and stores nothing.
+    //  dX: (row tid >> 2, block tid & 3), the d of each (d, s) pair (tid < 512).
+    //  W: half-block q = tid of the kMmqBN x 4-block weight tile: row q >> 3,
     //     block bb = (q >> 1) & 3, half h = q & 1.  Blocks pair up into 68-byte
     //     pairs (4-byte aligned): the even block's quants sit 2 bytes into the
     //     pair and are realigned from five dwords, the odd block's are aligned.
@@ -159,9 +170,11 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int q = tid + kMmqThreads * j;
-        xoff[j] = (uint32_t)((q >> 3) * k + 16 * (q & 7));
+        const bool live = kMmqThreads * (j + 1) <= 1024 || q < 1024;
+        xoff[j] = live ? (uint32_t)((q >> 3) * k + 16 * (q & 7)) : 0x80000000u;
     }
-    const uint32_t doff = (uint32_t)(((tid >> 2) * nb + (tid & 3)) * 8);
+    const bool dlive = kMmqThreads <= 4 * kMmqBM || tid < 4 * kMmqBM;
+    const uint32_t doff = dlive ? (uint32_t)(((tid >> 2) * nb + (tid & 3)) * 8) : 0x80000000u;
     const int wrow = tid >> 3, wbb = (tid >> 1) & 3, wh = tid & 1;
     const int wodd = wbb & 1;
     const int wsel = 2 * wodd + wh;           // 0: even h0, 1: even h1, 2: odd h0, 3: odd h1
@@ -185,14 +198,15 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 
         load_x(R, it);
         load_wd(R, it);
     };
-    auto store_x = [&](MmqStage &S, const MmqRegs &R) {
+    auto store_x = [&](MmqStageT &S, const MmqRegs &R) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int q = tid + kMmqThreads * j;
-            *reinterpret_cast<u32x4 *>(S.x + (q >> 3) * kMmqStride + 16 * (q & 7)) = R.x[j];
+            if (kMmqThreads * (j + 1) <= 1024 || q < 1024)
+                *reinterpret_cast<u32x4 *>(S.x + (q >> 3) * kMmqStride + 16 * (q & 7)) = R.x[j];
         }
     };
-    auto store_wd = [&](MmqStage &S, const MmqRegs &R) {
+    auto store_wd = [&](MmqStageT &S, const MmqRegs &R) {
         // even block: quants = bytes 2.. of dwords (w[0..3], w4); odd: w itself
         u32x4 qv;
         qv[0] = __builtin_amdgcn_alignbit(R.w[1], R.w[0], 16u);
@@ -202,9 +216,9 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 
         if (wodd) qv = R.w;
         *reinterpret_cast<u32x4 *>(S.w + wrow * kMmqStride + 64 * wh + 16 * wbb) = qv;
         if (wh == 0) S.dw[wbb][wrow] = half_bits_to_float(wodd ? (R.w4 >> 16) : (R.w[0] & 0xFFFFu));
-        S.dx[tid & 3][tid >> 2] = R.dx;
+        if (dlive) S.dx[tid & 3][tid >> 2] = R.dx;
     };
-    auto store_iter = [&](MmqStage &S, const MmqRegs &R) {
+    auto store_iter = [&](MmqStageT &S, const MmqRegs &R) {
         store_x(S, R);
         store_wd(S, R);
     };
@@ -232,13 +246,13 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 
         }
     };
     struct Ops { v4i A, B; };
-    auto rd = [&](const MmqStage &S, int b) -> Ops {
+    auto rd = [&](const MmqStageT &S, int b) -> Ops {
         Ops o;
         o.A = *reinterpret_cast<const v4i *>(S.x + arow * kMmqStride + 16 * khalf + 32 * b);
         o.B = *reinterpret_cast<const v4i *>(S.w + brow * kMmqStride + 64 * khalf + 16 * b);
         return o;
     };
-    auto rs = [&](const MmqStage &S, int p, float &sa, float &sb) {
+    auto rs = [&](const MmqStageT &S, int p, float &sa, float &sb) {
         sa = S.dx[2 * p + khalf][arow];
         sb = S.dw[2 * p + khalf][brow];
     };
@@ -285,7 +299,7 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 
     // per-lane base plus an immediate.
     auto stage = [&](int it, int cur) {
         const int nx = min(it + 2, last);
-        const MmqStage &S = st[cur];
+        const MmqStageT &S = st[cur];
         const v32f P01 = scale2(sa01, sb01);
         const BlockSum S0 = block_sum(o0.A, o0.B);
         const Ops o1 = rd(S, 1);
@@ -304,7 +318,7 @@ __global__ __launch_bounds__(kMmqThreads) __attribute__((amdgpu_waves_per_eu(4, 
         store_wd(st[cur ^ 1], R);
         load_wd(R, nx);
         __syncthreads();
-        const MmqStage &Sn = st[cur ^ 1];
+        const MmqStageT &Sn = st[cur ^ 1];
         o0 = rd(Sn, 0);
         rs(Sn, 0, sa01, sb01);
         const BlockSum S3 = block_sum(o3.A, o3.B);
@@ -603,26 +617,39 @@ static int launch_mmq(const uint8_t *w, int64_t w_row_bytes, const int8_t *xq, c
     // per-workgroup offsets are 32-bit: up to 256 rows of activations and 160
     // of weights (an offset with bit 31 set marks a load that reads nothing)
     if ((int64_t)kWideBM * k > 0x7FFFFFF0ll || (int64_t)kWideBN * w_row_bytes > 0x7FFFFFF0ll) return BQM_EUNSUPPORTED;
-    const int64_t tiles = (int64_t)((n + kMmqBN - 1) / kMmqBN) * ((m + kMmqBM - 1) / kMmqBM);
-    const int64_t wide = (int64_t)((n + kWideBN - 1) / kWideBN) * ((m + kWideBM - 1) / kWideBM);
-    if (tiles > 0x7FFFFFFF) return BQM_EUNSUPPORTED;
-    // Tile choice, counted in 32 x 32 tiles per SIMD: a wide workgroup gives
-    // each SIMD of its CU 10 tiles, one workgroup per CU per round; the
-    // 128 x 64 kernel runs two workgroups per CU, 4 tiles per SIMD per round.
-    // The wide tile does about 5% less work per tile, but only in whole rounds
-    // (a partial last round leaves CUs idle for a whole wide workgroup), so it
-    // is taken only where its rounds cost less.
+    const int64_t mt = (m + kMmqBM - 1) / kMmqBM;
+    const int64_t tiles64 = (int64_t)((n + 63) / 64) * mt;
+    const int64_t tiles96 = (int64_t)((n + 95) / 96) * mt;
+    const int64_t wide = (int64_t)((n + 160 - 1) / 160) * ((m + 256 - 1) / 256);
+    if (tiles64 > 0x7FFFFFFF) return BQM_EUNSUPPORTED;
+    // Tile choice by the busiest CU's time: workgroups per CU (rounded up) x
+    // 32 x 32 tiles per SIMD per workgroup x the measured time of one such
+    // tile for all of K=4096 (in 0.1 us at m=512; the ratios are what count):
+    //  * 128 x 64 (8 waves, two workgroups per CU): 2 tiles per SIMD, 15.5
+    //    with one workgroup on the CU, 13 with two;
+    //  * 128 x 96 (12 waves, one per CU): 3 tiles per SIMD, 14.5;
+    //  * 256 x 160 (8 waves, one per CU): 10 tiles per SIMD, 12.3.
+    // The 96-row tile takes shapes whose 64-row workgroups would leave some
+    // CUs a second workgroup in one round (N = 5152 or 6144 at m = 512: 42.8
+    // and 45.7 us against 53.5 and 55.7), the wide tile whole rounds of large
+    // N (20480).  All three fold in the same order: bitwise the same y.
     const int64_t cus = device_cus();
-    const int64_t cost_wide = (wide + cus - 1) / cus * 95;   // 10 tiles x 0.95, in tenths
-    const int64_t cost_tall = tiles * 40 / (2 * cus);         // 4 tiles per SIMD-round, fractional rounds
+    const int64_t r64 = (tiles64 + cus - 1) / cus, r96 = (tiles96 + cus - 1) / cus, rw = (wide + cus - 1) / cus;
+    const int64_t cost64 = r64 == 1 ? 2 * 155 : r64 * 2 * 130;
+    const int64_t cost96 = r96 * 3 * 145;
+    const int64_t costw = rw * 10 * 123;
     // the wide tile's output offsets ((256 + 32) rows of y, and a dead column
     // offset of 2^31 plus 27 rows) stay in 32 bits
-    if (cost_wide < cost_tall && (int64_t)(kWideBM + 32) * n * 4 <= 0x7FFFFFF0ll) {
-        hipLaunchKernelGGL((q8_0_gemm_wide_kernel<F8ACC>), dim3((unsigned)wide), dim3(kWideThreads), 0,
-                           as_stream(stream), w, w_row_bytes, xq, xds, y, m, k, n);
+    const bool wide_ok = (int64_t)(256 + 32) * n * 4 <= 0x7FFFFFF0ll;
+    if (wide_ok && costw < cost64 && costw < cost96) {
+        hipLaunchKernelGGL((q8_0_gemm_wide_kernel<F8ACC>), dim3((unsigned)wide), dim3(512), 0, as_stream(stream), w,
+                           w_row_bytes, xq, xds, y, m, k, n);
+    } else if (cost96 < cost64) {
+        hipLaunchKernelGGL((q8_0_gemm_kernel<F8ACC, 3>), dim3((unsigned)tiles96), dim3(768), 0, as_stream(stream), w,
+                           w_row_bytes, xq, xds, y, m, k, n);
     } else {
-        hipLaunchKernelGGL((q8_0_gemm_kernel<F8ACC>), dim3((unsigned)tiles), dim3(kMmqThreads), 0,
-                           as_stream(stream), w, w_row_bytes, xq, xds, y, m, k, n);
+        hipLaunchKernelGGL((q8_0_gemm_kernel<F8ACC, 2>), dim3((unsigned)tiles64), dim3(512), 0, as_stream(stream), w,
+                           w_row_bytes, xq, xds, y, m, k, n);
     }
     return launch_status();
 }

@@ -316,6 +316,34 @@ def test_gemm_wide_tile_stage_counts(bqm, k):
     assert_fold_close(y.cpu().numpy(), y_ref, T, f"gemm wide tile k={k}")
 
 
+# The 128-token x 96-row MMQ tile (12 waves, one workgroup per CU) is taken
+# where 128 x 64 workgroups would leave some CUs a second one in a round
+# (N around 5152 at m=512).  m=500: the last token tile holds 116 of 128;
+# n=5000: the last of 53 row tiles holds 8 of 96 rows; rows padded by 32 bytes.
+def test_gemm_96_row_tile_ragged_padded(bqm):
+    y, y_ref, T = q8_0_case(bqm, bqm.bqm_q8_0_gemm, 500, 1280, 5000, seed=78, pad=32, outliers=True)
+    assert_fold_close(y, y_ref, T, "gemm 96-row tile, ragged m and n, padded rows")
+
+
+# The three MMQ tiles fold every output's blocks in the same order, so the
+# columns an N=20480 call (256 x 160 tile), an N=16384 call (128 x 64) and an
+# N=5152 call (128 x 96) share are bitwise the same.
+def test_gemm_tiles_bitwise_same(bqm):
+    rng = np.random.default_rng(79)
+    m, k = 512, 1024
+    w = dev(workloads.q8_0_weights(20480, k, rng))
+    x = workloads.activations(m, k, rng, outliers=True)
+    xq, xds = bqm.bqm_q8_1_quantize(dev(x))
+    ys = {}
+    for n in (20480, 16384, 5152):
+        y = nan_like_out(m, n)
+        bqm.bqm_q8_0_gemm(w[:n].contiguous(), xq, xds, y)
+        ys[n] = y
+    torch.cuda.synchronize()
+    for n in (16384, 5152):
+        assert torch.equal(ys[n].view(torch.int32), ys[20480][:, :n].contiguous().view(torch.int32)), f"N={n}"
+
+
 def test_gemm_wide_tile_ragged_padded(bqm):
     # m=500: the second token half holds 244 of 256 tokens; n=20400: the last
     # of 128 row blocks holds 80 of 160 rows; rows padded by 32 bytes
