@@ -388,19 +388,22 @@ constexpr int kWideNC = kWideSB / 4;       // weight chunks (4 blocks) per stage
 constexpr int kWideNW = (2 * 4 * kWideBN + kWideThreads - 1) / kWideThreads;   // half-block slots per thread and chunk
 constexpr int kWideRS = kWideThreads / 8;  // rows between a thread's slots
 
-// One 256-k stage of the weight tile in LDS: per row the first 16 bytes of
-// blocks 0..7, then their second 16 bytes; the scale rows padded by 4 floats.
-struct WideStage {
-    uint8_t w[kWideBN * kWideStride];
-    float dw[kWideSB][kWideBN + 4];
+// The three 256-k stages of the weight tile in LDS.  A stage's quants: per
+// row the first 16 bytes of blocks 0..7, then their second 16 bytes.  Its
+// scale rows, padded by 4 floats, sit with the other stages' at the start
+// (15.4 KB), so one per-lane base with an immediate offset reaches every
+// scale of every stage.
+struct WideLds {
+    float dw[3][kWideSB][kWideBN + 4];
+    uint8_t w[3][kWideBN * kWideStride];
 };
-static_assert(3 * sizeof(WideStage) <= 160 * 1024, "LDS");
+static_assert(sizeof(WideLds) <= 160 * 1024 && sizeof(float) * 3 * kWideSB * (kWideBN + 4) < 65536, "LDS");
 
 template <bool F8ACC>
 __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void q8_0_gemm_wide_kernel(
     const uint8_t *__restrict__ w, int64_t w_row_bytes, const int8_t *__restrict__ xq, const float *__restrict__ xds,
     float *__restrict__ y, int m, int k, int n) {
-    __shared__ __attribute__((aligned(16))) WideStage st[3];
+    __shared__ __attribute__((aligned(16))) WideLds lds;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -454,12 +457,12 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2,
             Wr.d[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rW, (wod + ro) | dead, sw, 0);
         }
     };
-    auto store_w = [&](WideStage &S, const WRegs &Wr, int c) {
+    auto store_w = [&](int b, const WRegs &Wr, int c) {
 #pragma unroll
         for (int j = 0; j < kWideNW; j++) {
             if (tid + kWideThreads * j < 8 * kWideBN) {
-                *reinterpret_cast<u32x4 *>(S.w + wlds + kWideRS * kWideStride * j + 64 * c) = Wr.q[j];
-                if (hh0 == 0) (&S.dw[0][0])[wdw + kWideRS * j + 4 * c * (kWideBN + 4)] = half_bits_to_float(Wr.d[j]);
+                *reinterpret_cast<u32x4 *>(lds.w[b] + wlds + kWideRS * kWideStride * j + 64 * c) = Wr.q[j];
+                if (hh0 == 0) (&lds.dw[b][0][0])[wdw + kWideRS * j + 4 * c * (kWideBN + 4)] = half_bits_to_float(Wr.d[j]);
             }
         }
     };
@@ -514,12 +517,12 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2,
         v4i b0, b1;
         float sb;
     };
-    auto rdb = [&](const WideStage &S, int p, int j) -> BOps {
+    auto rdb = [&](int b, int p, int j) -> BOps {
         BOps o;
         const int brow = 32 * j + t;
-        o.b0 = *reinterpret_cast<const v4i *>(S.w + brow * kWideStride + 16 * kWideSB * khalf + 16 * (2 * p));
-        o.b1 = *reinterpret_cast<const v4i *>(S.w + brow * kWideStride + 16 * kWideSB * khalf + 16 * (2 * p + 1));
-        o.sb = S.dw[2 * p + khalf][brow];
+        o.b0 = *reinterpret_cast<const v4i *>(lds.w[b] + brow * kWideStride + 16 * kWideSB * khalf + 16 * (2 * p));
+        o.b1 = *reinterpret_cast<const v4i *>(lds.w[b] + brow * kWideStride + 16 * kWideSB * khalf + 16 * (2 * p + 1));
+        o.sb = lds.dw[b][2 * p + khalf][brow];
         return o;
     };
 
@@ -530,7 +533,7 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
     for (int c = 0; c < kWideNC; c++) {
         load_w(Wr, 0, c);
-        store_w(st[0], Wr, c);
+        store_w(0, Wr, c);
     }
 #pragma unroll
     for (int p = 0; p < kWideSB / 2; p++) load_a(p, 0);
@@ -541,27 +544,30 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2,
     // registers into st[nxt] at pair 2c, and the next chunk's loads are issued
     // in its place (past the end they repeat the last stage, so the compiler's
     // count of loads in flight stays exact).
-    BOps o = rdb(st[0], 0, 0);
+    BOps o = rdb(0, 0, 0);
     auto stage = [&](int it, int cur, int nxt) {
-        const WideStage &S = st[cur];
 #pragma unroll
         for (int p = 0; p < kWideSB / 2; p++) {
 #pragma unroll
             for (int j = 0; j < kWideR; j++) {
                 const BOps c = o;
-                if (j + 1 < kWideR) o = rdb(S, p, j + 1);
-                else if (p + 1 < kWideSB / 2) o = rdb(S, p + 1, 0);
-                else o = rdb(st[nxt], 0, 0);   // complete since this stage's barrier
+                if (j + 1 < kWideR) o = rdb(cur, p, j + 1);
+                else if (p + 1 < kWideSB / 2) o = rdb(cur, p + 1, 0);
+                else o = rdb(nxt, 0, 0);   // complete since this stage's barrier
                 const v32f P = scale2(D[p], c.sb);
                 const BlockSum S0 = block_sum(A[2 * p], c.b0);
                 const BlockSum S1 = block_sum(A[2 * p + 1], c.b1);
                 fold(acc[j], S0, P, 0);
                 fold(acc[j], S1, P, 1);
                 asm volatile("" : "+v"(acc[j]) :: "memory");
+                // Each tile step is scheduled on its own: interleaving steps
+                // made the compiler spill (6 VGPRs in the int8 arm, 14 in the
+                // f32 arm, each reload waiting for every load in flight).
+                __builtin_amdgcn_sched_barrier(0);
                 if (j == kWideR - 1) load_a(p, min(it + 1, last));
                 if (j == 0 && (p & 1) == 0) {
                     const int ch = p / 2;
-                    store_w(st[nxt], Wr, ch);
+                    store_w(nxt, Wr, ch);
                     if (ch + 1 < kWideNC) load_w(Wr, min(it + 1, last), ch + 1);
                     else load_w(Wr, min(it + 2, last), 0);
                     if (ch + 1 == kWideNC) __syncthreads();
