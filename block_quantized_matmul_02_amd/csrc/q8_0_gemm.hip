@@ -526,17 +526,20 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(2,
         return o;
     };
 
-    // Prologue: stage 0 into st[0], its activations into the registers, and
-    // the first chunk of stage 1 into the weight registers.
+    // Prologue: stage 0 into st[0] (both chunks loaded before either is
+    // stored: one wait for memory instead of two), its activations into the
+    // registers, and the first chunk of stage 1 into the weight registers.
     WRegs Wr;
     const int last = nit - 1;
+    {
+        WRegs W1;
+        load_w(Wr, 0, 0);
+        load_w(W1, 0, 1);
 #pragma unroll
-    for (int c = 0; c < kWideNC; c++) {
-        load_w(Wr, 0, c);
-        store_w(0, Wr, c);
+        for (int p = 0; p < kWideSB / 2; p++) load_a(p, 0);
+        store_w(0, Wr, 0);
+        store_w(0, W1, 1);
     }
-#pragma unroll
-    for (int p = 0; p < kWideSB / 2; p++) load_a(p, 0);
     load_w(Wr, min(1, last), 0);
     __syncthreads();
 
