@@ -319,10 +319,13 @@ def test_gemm_wide_tile_stage_counts(bqm, k):
 # The 128-token x 96-row MMQ tile (12 waves, one workgroup per CU) is taken
 # where 128 x 64 workgroups would leave some CUs a second one in a round
 # (N around 5152 at m=512).  m=500: the last token tile holds 116 of 128;
-# n=5000: the last of 53 row tiles holds 8 of 96 rows; rows padded by 32 bytes.
-def test_gemm_96_row_tile_ragged_padded(bqm):
-    y, y_ref, T = q8_0_case(bqm, bqm.bqm_q8_0_gemm, 500, 1280, 5000, seed=78, pad=32, outliers=True)
-    assert_fold_close(y, y_ref, T, "gemm 96-row tile, ragged m and n, padded rows")
+# n=5000: the last of 53 row tiles holds 8 of 96 rows; m=100, n=20000: one
+# partial token tile (100 of 128) over 209 row tiles, the last 32 rows; rows
+# padded by 32 bytes.
+@pytest.mark.parametrize("m,k,n", [(500, 1280, 5000), (100, 512, 20000)])
+def test_gemm_96_row_tile_ragged_padded(bqm, m, k, n):
+    y, y_ref, T = q8_0_case(bqm, bqm.bqm_q8_0_gemm, m, k, n, seed=78, pad=32, outliers=True)
+    assert_fold_close(y, y_ref, T, f"gemm 96-row tile {m}x{k}x{n}, ragged m and n, padded rows")
 
 
 # The three MMQ tiles fold every output's blocks in the same order, so the
