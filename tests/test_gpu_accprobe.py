@@ -98,6 +98,18 @@ def test_f8acc_wide_tile(bqm, dist):
     check(run(bqm, w, xq, xds), y_ref, T, f"f8acc wide tile {dist}", tolerance(k))
 
 
+@pytest.mark.parametrize("dist", ["wide", "mid"])
+def test_f8acc_96_row_tile(bqm, dist):
+    # m=512, N=5152: the MMQ's 128-token x 96-row tile (12 waves), with the f32
+    # arm's block sums; the last row tile holds 64 of 96 rows
+    m, k, n = 512, 512, 5152
+    rng = np.random.default_rng(4100)
+    w = workloads.accprobe_weights(n, k, rng, dist)
+    xq, xds = workloads.accprobe_activations(m, k, rng, dist)
+    y_ref, T = oracle.q8_0_matmul_e4m3(w, xq, xds, k)
+    check(run(bqm, w, xq, xds), y_ref, T, f"f8acc 96-row tile {dist}", tolerance(k))
+
+
 def test_f8acc_group_truncation_as_measured(bqm):
     # 448 plus one small product in the same 8-value lane group keeps only
     # multiples of 2^-5; in the other lane half it is added exactly.  This

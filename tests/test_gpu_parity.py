@@ -279,14 +279,15 @@ def test_gemm_full_size_workloads(bqm, n):
     assert_fold_close(y.cpu().numpy(), y_ref, T, f"gemm full n={n}")
 
 
+@pytest.mark.parametrize("n", [4096, 5152])
 @pytest.mark.parametrize("k", [256, 1280, 768, 512])
-def test_gemm_iteration_counts(bqm, k):
-    # m=512, N=4096: 64 column tiles x 4 token tiles.  The MMQ's loop covers
-    # two 128-k stages per trip: K=256 is one trip (prologue and both LDS
-    # buffers only), 512 two, 768 three and 1280 five; every output against
-    # the oracle.
-    rng = np.random.default_rng(k)
-    m, n = 512, 4096
+def test_gemm_iteration_counts(bqm, k, n):
+    # m=512, N=4096: 64 column tiles x 4 token tiles of 128 x 64; N=5152: 54 x 4
+    # tiles of 128 x 96.  The loop covers two 128-k stages per trip: K=256 is
+    # one trip (prologue and both LDS buffers only), 512 two, 768 three and
+    # 1280 five; every output against the oracle.
+    rng = np.random.default_rng(k + n)
+    m = 512
     w = workloads.q8_0_weights(n, k, rng)
     x = workloads.activations(m, k, rng, outliers=True)
     xq, xds, xq_ref, xds_ref = quantize_both(bqm, x)
@@ -294,7 +295,7 @@ def test_gemm_iteration_counts(bqm, k):
     bqm.bqm_q8_0_gemm(dev(w), xq, xds, y)
     torch.cuda.synchronize()
     y_ref, T = oracle.q8_0_matmul(w, xq_ref, xds_ref, k)
-    assert_fold_close(y.cpu().numpy(), y_ref, T, f"gemm iterations k={k}")
+    assert_fold_close(y.cpu().numpy(), y_ref, T, f"gemm iterations k={k} n={n}")
 
 
 # The 256-token x 160-row MMQ tile (one workgroup per CU) is the one the
