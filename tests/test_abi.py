@@ -224,3 +224,17 @@ def test_product_path_never_touches_the_oracle():
             if fname.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, fname)).read()
                 assert not re.search(r"\boracle\b", text), f"{fname} mentions the oracle"
+
+
+def test_missing_library_raises(monkeypatch):
+    # No CPU fallback: without the built library every call fails loudly, and
+    # host tensors are refused rather than computed on the CPU.
+    import torch
+    import block_quantized_matmul_02_amd as bqm
+    monkeypatch.setattr(bqm, "LIB_PATH", os.path.join(PKG, "no_such_libbqmm.so"))
+    monkeypatch.setattr(bqm, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        bqm.lib()
+    with pytest.raises((RuntimeError, ValueError)):
+        bqm.bqm_q8_1_quantize(torch.zeros(1, 32))
+
