@@ -60,16 +60,18 @@
 //  * XCD-aware tile order (below), and range-checked buffer loads: ragged m
 //    and n tails read zeros (zero scales), and only in-range outputs are
 //    stored.
-//  * Measured (m=512, K=4096, weights rotated past the cache, interleaved on
+//  * Measured with the 128 x 64 tile at every N, before the other two tiles
+//    existed (m=512, K=4096, weights rotated past the cache, interleaved on
 //    one box): N=20480 140 us against 167 for a 16-wave, one-workgroup-per-CU
 //    version (two k-groups over alternate stages, their partial sums added in
 //    LDS at the end), N=5152 52 against 58, N=4096 34 against 35.  Ablations
-//    at N=20480: without the global loads 126 us, also without the LDS stores
-//    106, also without the barriers 102 (the register-only floor is about
-//    75).  Tried and not kept: direct global-to-LDS loads of the activation
-//    tile (XOR-swizzled 128-byte rows) and its d values, which removed two of
-//    the three 16-byte LDS stores per thread and stage: bitwise the same, but
-//    152 us against 140.
+//    of that tile at N=20480: without the global loads 126 us, also without
+//    the LDS stores 106, also without the barriers 102 (the register-only
+//    floor is about 75).  Tried and not kept: direct global-to-LDS loads of
+//    the activation tile (XOR-swizzled 128-byte rows) and its d values, which
+//    removed two of the three 16-byte LDS stores per thread and stage:
+//    bitwise the same, but 152 us against 140.  The wide tile below now
+//    takes N=20480 (120-123 us) and the 96-row tile N=5152 (40-41 us).
 //
 // The same kernel with its accumulator as the one free variable is the
 // accumulator instrument ("accprobe_bench.rs" page, memra-engine 0.124.1,
