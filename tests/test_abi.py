@@ -238,3 +238,43 @@ def test_missing_library_raises(monkeypatch):
     with pytest.raises((RuntimeError, ValueError)):
         bqm.bqm_q8_1_quantize(torch.zeros(1, 32))
 
+
+
+# --------------------------------------------------------------------------- size limits
+# Each kernel addresses a workgroup's rows with 32-bit buffer offsets and
+# launches a grid of bounded dimensions; sizes past those limits are refused
+# with BQM_EUNSUPPORTED before anything is launched (the stand-in pointers are
+# never dereferenced).
+
+BIG_M = 65536 * 128      # 65,536 token tiles of 128: one more than a grid's y dimension holds
+
+
+def test_q8_0_size_limits(L):
+    k = 256 * 32769                                  # 256 activation rows of k bytes pass 2^31
+    rb = k // 32 * 34
+    for fn in (L.bqm_q8_0_gemm, L.bqm_q8_0_gemm_f8acc):
+        assert fn(A16, rb, B16, C16, D16, 16, k, 8, NUL) == 2
+        assert fn(A16, 13421776, B16, C16, D16, 16, 4096, 8, NUL) == 2        # 160 weight rows pass 2^31
+        assert fn(A16, 272, B16, C16, D16, 2 ** 31 - 1, 256, 2 ** 31 - 1, NUL) == 2   # 2^31 tiles
+    assert L.bqm_q8_0_gemv(A16, 33554432, B16, C16, D16, 1, 4096, 8, NUL) == 2     # 64 rows pass 2^31
+    assert L.bqm_q8_0_gemv_f32(A16, 33554432, B16, D16, 1, 4096, 8, NUL) == 2
+
+
+def test_e4m3_size_limits(L):
+    F = ctypes.c_float
+    k = 128 * 52430                                  # 320 weight rows of k bytes pass 2^31
+    assert L.bqm_e4m3_gemm(A16, B16, C16, D16, 16, k, 8, NUL) == 2
+    assert L.bqm_e4m3_gemm(A16, B16, C16, D16, BIG_M, 128, 8, NUL) == 2
+    assert L.bqm_e4m3_gemm_exact(A16, B16, C16, D16, BIG_M, 128, 8, NUL) == 2
+    assert L.bqm_e4m3_gemv(A16, B16, F(1.0), D16, 1, 4096, 33554432, NUL) == 2    # n*k past 2^37
+    kb = 16 * 419431
+    assert L.bqm_e4m3_blk_gemm(A16, B16, C16, D16, A16, 16, kb, 8, NUL) == 2
+    assert L.bqm_e4m3_blk_gemm(A16, B16, C16, D16, A16, BIG_M, 128, 8, NUL) == 2
+    assert L.bqm_e4m3_blk_quantize(A16, B16, C16, 2 ** 31 - 1, 16384, NUL) == 2   # 2^31 workgroups
+
+
+def test_f16_mirror_size_limits(L):
+    assert L.bqm_f16_gemm(A16, B16, C16, 16, 8388608, 8, NUL) == 2                 # 128 rows of 2k bytes
+    assert L.bqm_f16_gemm(A16, B16, C16, BIG_M, 64, 8, NUL) == 2
+    k = 2 ** 31 - 64
+    assert L.bqm_q8_0_dequant_f16(A16, k // 32 * 34, B16, k, 2 ** 31 - 1, NUL) == 2   # 2^31 workgroups
