@@ -111,3 +111,38 @@ def test_graph_replays_match_eager(bqm):
         torch.cuda.synchronize()
         for name, ref in eager.items():
             assert torch.equal(graph_bufs[name], ref), f"replay {rep}: {name} differs from the eager launch"
+
+
+def test_two_streams_at_once_match_serial(bqm):
+    # The library keeps no state between calls and uses no memory beyond the
+    # caller's buffers, so the same calls issued on two streams at once (each
+    # with its own buffers) give the serial results bit for bit; the stream
+    # argument orders the work (the reads below wait on each stream's event).
+    dev = "cuda:0"
+    rng = np.random.default_rng(78)
+    k = 4096
+    w = torch.from_numpy(workloads.q8_0_weights(5000, k, rng)).to(dev)
+    codes, ws = workloads.e4m3_weights(3000, k, rng)
+    w8 = torch.from_numpy(codes).to(dev)
+    xs = [torch.from_numpy(workloads.activations(m, k, rng, outliers=True)).to(dev) for m in (1, 9, 300)]
+
+    def work(x1, x9, x300):
+        xq, xd = bqm.bqm_q8_1_quantize(x300)
+        q8, sc = bqm.bqm_e4m3_quantize_amax(x300, ws)
+        return [bqm.bqm_q8_0_gemv_f32(w, x1), bqm.bqm_e4m3_gemv(w8, x9, ws),
+                bqm.bqm_q8_0_gemm(w, xq, xd), bqm.bqm_e4m3_gemm(w8, q8, sc), bqm.bqm_e4m3_gemm_exact(w8, q8, sc)]
+
+    serial = work(*xs)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    out = {}
+    for _ in range(3):
+        for name, s in (("a", s1), ("b", s2)):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                out[name] = work(*xs)
+        for s in (s1, s2):
+            torch.cuda.current_stream().wait_stream(s)
+        for name in ("a", "b"):
+            for i, (got, ref) in enumerate(zip(out[name], serial)):
+                assert torch.equal(got.view(torch.int32), ref.view(torch.int32)), f"stream {name}, call {i}"
