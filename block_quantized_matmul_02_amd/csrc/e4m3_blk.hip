@@ -261,9 +261,16 @@ __global__ __launch_bounds__(kB8Threads) void e4m3_blk_gemm_kernel(const uint8_t
             const float sxt = S.xs[wm * 32 + (lane & 31)];
             struct BT { v8i b0, b1; };
             auto rdt = [&](int j) -> BT { return BT{ld8(pb + j * 32 * kB8RowStride), ld8(pb + j * 32 * kB8RowStride + 64)}; };
+            // The pair of MFMAs is issued at raised wave priority, so that
+            // the other wave of the SIMD, busy with its fold, does not delay
+            // their issue (interleaved at m=512, K=4096: N=20480 65.8 ->
+            // 63.3 us, N=16384 57.0 -> 56.4; bitwise the same results).
             auto part = [&](const BT &b) {
+                __builtin_amdgcn_s_setprio(1);
                 v16f P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b.b0, a0, z, 0, 0, 0, 127, 0, 127);
-                return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b.b1, a1, P, 0, 0, 0, 127, 0, 127);
+                P = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b.b1, a1, P, 0, 0, 0, 127, 0, 127);
+                __builtin_amdgcn_s_setprio(0);
+                return P;
             };
             // Three partial sets, indexed at compile time: tiles j+1 and j+2
             // are on the matrix cores while tile j is folded; the operands of
