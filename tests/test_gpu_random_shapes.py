@@ -71,6 +71,8 @@ E4M3_GEMV_SHAPES = draw(9007, 10, (1, 16), 256, (256, 8192), (1, 30000), 2.0e9)
 BLK_Q_SHAPES = draw(9008, 10, (1, 3000), 16, (16, 8192), budget=2.0e7)
 BLK_GEMM_SHAPES = draw(9009, 10, (1, 1100), 16, (16, 4096), (1, 24000), 3.0e9)
 F16_GEMM_SHAPES = draw(9010, 8, (1, 1100), 64, (64, 4096), (1, 24000), 3.0e9)
+F8ACC_SHAPES = draw(9011, 8, (1, 1100), 256, (256, 4096), (1, 24000), 3.0e9)
+NAN_COUNTS = [int(c) for c in np.random.default_rng(9012).integers(1, 50_000_000, size=6)]
 
 
 def ids(shapes):
@@ -119,6 +121,10 @@ def exact_bound(k):      # fp16 matrix cores, exact code conversion
 
 def blk_bound(k):        # fp8 matrix core per 128-k block, f32 folds
     return 7 * 2.0 ** -13 + ((k + 127) // 128 + 18) * 2.0 ** -24
+
+
+def f8acc_bound(k):      # two 16-deep fp8 MFMAs per 32-block, f32 folds
+    return 7 * 2.0 ** -13 + (k // 32 + 4) * 2.0 ** -24
 
 
 def padded_q8_0(n, k, rng):
@@ -281,3 +287,28 @@ def test_random_f16_mirror(bqm, m, k, n):
     assert np.array_equal(x16.view(torch.int16).cpu().numpy().view(np.uint16), x16_ref)
     y_ref, T = oracle.f16_gemm(w16_ref, x16_ref)
     close(y.cpu().numpy(), y_ref, T, f"f16 mirror {m}x{k}x{n}")
+
+
+# ---------------------------------------------------------------- instrument and NaN scan
+
+
+@pytest.mark.parametrize("dist", ["wide", "mid"])
+@pytest.mark.parametrize("m,k,n", F8ACC_SHAPES, ids=ids(F8ACC_SHAPES))
+def test_random_f8acc(bqm, m, k, n, dist):
+    rng = np.random.default_rng(m * 7 + k * 3 + n + 11)
+    w = workloads.accprobe_weights(n, k, rng, dist)
+    xq, xds = workloads.accprobe_activations(m, k, rng, dist)
+    y = nan_out(m, n)
+    bqm.bqm_q8_0_gemm_f8acc(dev(w), dev(xq), dev(xds), y)
+    torch.cuda.synchronize()
+    y_ref, T = oracle.q8_0_matmul_e4m3(w, xq, xds, k)
+    worst = close(y.cpu().numpy(), y_ref, T, f"f8acc {m}x{k}x{n} {dist}", tol=f8acc_bound(k))
+    print(f"f8acc {m}x{k}x{n} {dist}: max err/T = {worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("count", NAN_COUNTS)
+def test_random_nan_count(bqm, count):
+    rng = np.random.default_rng(count)
+    b = rng.integers(0, 256, size=count, dtype=np.uint8)
+    got = bqm.bqm_e4m3_nan_count(dev(b)).item()
+    assert got == oracle.e4m3_nan_count(b)
